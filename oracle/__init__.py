@@ -1,0 +1,39 @@
+"""Plain CPU fp64 oracle for block-sparse attention scoring.
+
+TEST INFRASTRUCTURE ONLY.  Only ``tests/``, ``__graft_entry__.smoke()`` and the
+``cpu_baseline`` leg of ``bench.py`` may import or call anything in this
+package.  The HIP library never imports it and shares no code with it.
+
+Every function works on fp64 NumPy arrays holding the exact values of the
+inputs (bf16 or fp32 values upcast to fp64), follows the definition written
+on the pages step by step, and uses no blocking, fusion or reordering beyond
+that definition:
+
+* ``scoring``   - PARK's query-preserving block scorer (PARK: Accurate Block
+  Retrieval for Sparse Attention in Video Diffusion Transformers, Abstract).
+* ``selection`` - online top-p block selection with per-head thresholds
+  (HASTE abstract; HEART abstract).
+* ``attention`` - attention restricted to the retrieved blocks, written as
+  dense softmax attention under an explicit token mask (PARK, Abstract).
+* ``drift``     - the per-head query-key drift signal and the refresh rule of
+  Temporal Mask Reuse (HEART abstract; HASTE abstract).
+* ``trajectory``- estimate once, cache, reuse, refresh on drift (RAPID
+  abstract; HEART abstract), plus RAPID's Turbo re-selection on cached scores.
+
+What pins each function (closed forms, invariants, brute force, independent
+library routines) is in ``tests/test_oracle.py``; no function here is left
+parity-unpinned.
+"""
+from .blocks import block_bounds, num_blocks
+from .scoring import pool_keys, score_blocks, score_blocks_pooled_query, score_head
+from .selection import select_row, select_topp, density
+from .attention import block_sparse_attention, token_mask
+from .drift import drift, refresh_decision
+from .trajectory import cache_trajectory, turbo_schedule
+
+__all__ = [
+    "block_bounds", "num_blocks", "pool_keys", "score_blocks", "score_head",
+    "score_blocks_pooled_query", "select_row", "select_topp", "density",
+    "block_sparse_attention", "token_mask", "drift", "refresh_decision",
+    "cache_trajectory", "turbo_schedule",
+]

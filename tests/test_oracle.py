@@ -1,0 +1,387 @@
+"""Pins of the fp64 oracle against what the pages and mathematics fix.
+
+Each test ties one oracle function to something other than itself: a
+hand-worked example, a closed form, an invariant, brute force on tiny inputs
+or an independent library routine (torch's float64 scaled_dot_product_attention
+and logsumexp).  A plausible slip in the oracle (a dropped term, a transposed
+operand, pooling queries before the softmax, an exclusive top-p boundary, a
+wrong tie order, a divisor of B instead of the ragged block size) fails at
+least one of them.
+"""
+import itertools
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand(shape, seed, scale=1.0):
+    return np.random.default_rng(seed).standard_normal(shape) * scale
+
+
+def _sdpa(q, k, v, mask=None, scale=None):
+    """torch float64 SDPA on CPU: an independent textbook attention."""
+    t = lambda a: torch.from_numpy(np.ascontiguousarray(a))[None, None]
+    m = None if mask is None else torch.from_numpy(mask)[None, None]
+    out = torch.nn.functional.scaled_dot_product_attention(t(q), t(k), t(v), attn_mask=m, scale=scale)
+    return out[0, 0].numpy()
+
+
+# ---------------------------------------------------------------- hand example
+
+def test_hand_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "hand_example.json")))
+    q = np.array(g["q"])[:, None]
+    k = np.array(g["k"])[:, None]
+    v = np.array(g["v"])[:, None]
+    b, sc = g["block"], g["scale"]
+    np.testing.assert_allclose(O.pool_keys(k, b)[:, 0], g["pooled_keys"], atol=0, rtol=0)
+    s = O.score_head(q, k, b, sc)
+    np.testing.assert_allclose(s, g["scores"], atol=1e-12)
+    for key, p in (("select_p07", 0.7), ("select_p05", 0.5)):
+        _, counts, lists = O.select_topp(s[None], [p])
+        assert [list(map(int, r)) for r in lists[0]] == g[key]["lists"]
+        assert list(counts[0]) == g[key]["counts"]
+    out, lse = O.block_sparse_attention(q, k, v, b, g["select_p07"]["lists"], scale=sc)
+    np.testing.assert_allclose(out[:, 0], g["attention_out"], atol=1e-12)
+    np.testing.assert_allclose(lse, g["attention_lse"], atol=1e-12)
+    f = g["drift_scale"]
+    d = O.drift((f * q)[None], (f * k)[None], q[None], k[None])
+    np.testing.assert_allclose(d, [g["drift_expected"]], rtol=1e-12)
+    assert list(O.refresh_decision(d, 0.05)) == [1]
+    assert list(O.refresh_decision(d, 0.2)) == [0]
+
+
+# ---------------------------------------------------------------- pooling
+
+def test_pool_blockwise_constant_keys_ragged():
+    n, b, d = 70, 16, 5                     # 5 blocks, last one holds 6 tokens
+    nb = O.num_blocks(n, b)
+    const = np.random.default_rng(1).integers(-64, 64, (nb, d)) / 8.0   # short dyadics: exact sums
+    k = np.repeat(const, b, axis=0)[:n]
+    np.testing.assert_array_equal(O.pool_keys(k, b), const)
+
+
+def test_pool_linear_ramp_closed_form():
+    n, b = 45, 8
+    k = np.arange(n, dtype=np.float64)[:, None] * np.array([[1.0, -2.0]])
+    got = O.pool_keys(k, b)
+    for j in range(O.num_blocks(n, b)):
+        lo, hi = j * b, min(n, j * b + b)
+        mid = (lo + hi - 1) / 2.0            # mean of lo..hi-1
+        np.testing.assert_allclose(got[j], [mid, -2 * mid], rtol=0, atol=1e-12)
+
+
+# ---------------------------------------------------------------- scoring
+
+@pytest.mark.parametrize("n,b,d", [(256, 64, 64), (100, 16, 8), (37, 8, 4)])
+def test_score_rows_are_distributions(n, b, d):
+    q, k = _rand((1, n, d), 2), _rand((1, n, d), 3)
+    s = O.score_blocks(q, k, b)[0]
+    assert (s >= 0).all()
+    np.testing.assert_allclose(s.sum(axis=1), 1.0, atol=1e-12)
+
+
+def test_score_zero_queries_is_uniform():
+    n, b, d = 90, 16, 8
+    s = O.score_blocks(np.zeros((1, n, d)), _rand((1, n, d), 4), b)[0]
+    np.testing.assert_allclose(s, 1.0 / O.num_blocks(n, b), atol=1e-15)
+
+
+def test_score_single_block_is_one():
+    s = O.score_blocks(_rand((2, 50, 8), 5), _rand((2, 50, 8), 6), 64)
+    np.testing.assert_allclose(s, 1.0, atol=1e-15)
+
+
+@pytest.mark.parametrize("n,b,d", [(96, 16, 8), (100, 16, 8)])
+def test_score_equals_sdpa_over_pooled_keys(n, b, d):
+    """Steps 2-4 against torch SDPA: softmax over pooled keys, one-hot values."""
+    q, k = _rand((n, d), 7, 2.0), _rand((n, d), 8, 2.0)
+    nb = O.num_blocks(n, b)
+    kbar = O.pool_keys(k, b)
+    per_query = _sdpa(q, kbar, np.eye(nb))           # [n, nb] softmax rows
+    want = np.stack([per_query[i * b:min(n, i * b + b)].mean(axis=0) for i in range(nb)])
+    np.testing.assert_allclose(O.score_head(q, k, b, 1 / math.sqrt(d)), want, atol=1e-13)
+
+
+def test_score_is_mean_dense_block_mass_for_blockwise_constant_keys():
+    """Keys constant per block and B | N: S is the dense attention mass per block.
+
+    The dense mass comes from torch SDPA over all tokens with block-indicator
+    values, so a transposed S, a wrong softmax axis, a missing scale or
+    pooling the queries before the softmax all fail here.
+    """
+    n, b, d = 128, 16, 8
+    nb = n // b
+    k = np.repeat(_rand((nb, d), 9, 1.5), b, axis=0)
+    q = _rand((n, d), 10, 2.0)
+    indicator = np.kron(np.eye(nb), np.ones((b, 1)))  # [n, nb]
+    mass = _sdpa(q, k, indicator)
+    want = mass.reshape(nb, b, nb).mean(axis=1)
+    got = O.score_head(q, k, b, 1 / math.sqrt(d))
+    np.testing.assert_allclose(got, want, atol=1e-13)
+    # pooling queries first (the mismatch PARK's abstract names) differs here
+    pooled = O.score_blocks_pooled_query(q[None], k[None], b)[0]
+    assert np.abs(pooled - want).max() > 1e-3
+
+
+def test_score_equal_queries_in_block_equals_pooled_query_scorer():
+    n, b, d = 112, 16, 8
+    nb = n // b
+    q = np.repeat(_rand((nb, d), 11, 2.0), b, axis=0)
+    k = _rand((n, d), 12, 2.0)
+    np.testing.assert_allclose(O.score_blocks(q[None], k[None], b),
+                               O.score_blocks_pooled_query(q[None], k[None], b), atol=1e-14)
+
+
+def test_pooled_query_scorer_equals_sdpa():
+    n, b, d = 100, 16, 8
+    q, k = _rand((n, d), 13, 2.0), _rand((n, d), 14, 2.0)
+    nb = O.num_blocks(n, b)
+    want = _sdpa(O.pool_keys(q, b), O.pool_keys(k, b), np.eye(nb))
+    np.testing.assert_allclose(O.score_blocks_pooled_query(q[None], k[None], b)[0], want, atol=1e-13)
+
+
+def test_score_brute_force_loops_tiny():
+    """Pure-Python loops with math.exp on a 1-head, 4-block case."""
+    n, b, d = 64, 16, 4
+    q, k = _rand((n, d), 15), _rand((n, d), 16)
+    sc = 1 / math.sqrt(d)
+    nb = n // b
+    want = [[0.0] * nb for _ in range(nb)]
+    for i_blk in range(nb):
+        for i in range(i_blk * b, i_blk * b + b):
+            logit = []
+            for j_blk in range(nb):
+                kb = [sum(k[t][c] for t in range(j_blk * b, j_blk * b + b)) / b for c in range(d)]
+                logit.append(sc * sum(q[i][c] * kb[c] for c in range(d)))
+            z = sum(math.exp(x) for x in logit)
+            for j_blk in range(nb):
+                want[i_blk][j_blk] += math.exp(logit[j_blk]) / z / b
+    np.testing.assert_allclose(O.score_head(q, k, b, sc), want, atol=1e-13)
+
+
+# ---------------------------------------------------------------- selection
+
+def _brute_force_topp(s, p):
+    """Minimum-size subsets with mass >= p; among them the max-mass one."""
+    nb = len(s)
+    if p >= 1.0:
+        return tuple(range(nb))
+    for size in range(1, nb + 1):
+        best, best_mass = None, -1.0
+        for sub in itertools.combinations(range(nb), size):
+            mass = sum(s[j] for j in sub)
+            if mass >= p and mass > best_mass:
+                best, best_mass = sub, mass
+        if best is not None:
+            return tuple(sorted(best))
+    return tuple(range(nb))
+
+
+@pytest.mark.parametrize("seed", range(40))
+def test_select_matches_subset_enumeration(seed):
+    rng = np.random.default_rng(100 + seed)
+    nb = int(rng.integers(1, 12))
+    s = rng.dirichlet(np.full(nb, 0.5))
+    p = float(np.float32(rng.uniform(0.05, 0.99)))
+    sel, kstar, _, _ = O.select_row(s, p)
+    assert tuple(int(x) for x in sel) == _brute_force_topp(s, p)
+    assert kstar == len(sel)
+
+
+def test_select_boundary_is_inclusive():
+    s = np.array([0.125, 0.5, 0.125, 0.25])      # dyadic: sums are exact
+    sel, kstar, _, _ = O.select_row(s, 0.75)
+    assert kstar == 2 and list(sel) == [1, 3]
+
+
+def test_select_zero_queries_ceil_rule_and_tie_order():
+    n, b, d = 160, 16, 8                           # NB = 10, uniform scores
+    s = O.score_blocks(np.zeros((1, n, d)), _rand((1, n, d), 17), b)[0]
+    for p in (0.05, 0.33, 0.71, 0.94):
+        kk = math.ceil(p * 10)
+        _, counts, lists = O.select_topp(s[None], [p])
+        assert (counts == kk).all()
+        for row in lists[0]:
+            assert list(row) == list(range(kk))     # equal scores: lower index first
+
+
+def test_select_monotone_in_p():
+    rng = np.random.default_rng(18)
+    s = rng.dirichlet(np.full(40, 0.3), size=20)
+    ps = [0.1, 0.3, 0.5, 0.7, 0.9, 0.99]
+    prev = None
+    for p in ps:
+        mask, _, _ = O.select_topp(s[None], [p])
+        if prev is not None:
+            assert (mask >= prev).all()
+        prev = mask
+
+
+def test_select_extremes_and_cap():
+    s = np.random.default_rng(19).dirichlet(np.ones(9), size=5)
+    m1, c1, _ = O.select_topp(s[None], [1.0])
+    assert (m1 == 1).all() and (c1 == 9).all()
+    m0, c0, l0 = O.select_topp(s[None], [0.0])
+    assert (c0 == 1).all()
+    for i in range(5):
+        assert int(l0[0][i][0]) == int(np.argmax(s[i]))
+    mc, cc, _ = O.select_topp(s[None], [0.99], max_blocks=3)
+    assert (cc <= 3).all() and (mc.sum(axis=-1) == cc).all()
+
+
+def test_density_counts_pairs():
+    counts = np.array([[1, 2, 3], [3, 3, 3]])
+    np.testing.assert_allclose(O.density(counts, 3), [6 / 9, 1.0])
+
+
+# ---------------------------------------------------------------- attention
+
+@pytest.mark.parametrize("n,b,d", [(128, 32, 16), (100, 16, 8)])
+def test_attention_full_list_equals_dense_sdpa(n, b, d):
+    q, k, v = _rand((n, d), 20, 1.5), _rand((n, d), 21, 1.5), _rand((n, d), 22)
+    nb = O.num_blocks(n, b)
+    lists = [list(range(nb))] * nb
+    out, lse = O.block_sparse_attention(q, k, v, b, lists)
+    np.testing.assert_allclose(out, _sdpa(q, k, v), atol=1e-13)
+    logits = torch.from_numpy(q @ k.T / math.sqrt(d))
+    np.testing.assert_allclose(lse, torch.logsumexp(logits, dim=1).numpy(), atol=1e-13)
+
+
+def test_attention_sparse_equals_masked_sdpa():
+    n, b, d = 100, 16, 8
+    nb = O.num_blocks(n, b)
+    rng = np.random.default_rng(23)
+    q, k, v = _rand((n, d), 24, 1.5), _rand((n, d), 25, 1.5), _rand((n, d), 26)
+    block_mask = rng.random((nb, nb)) < 0.4
+    block_mask[np.arange(nb), rng.integers(0, nb, nb)] = True
+    lists = [np.flatnonzero(block_mask[i]) for i in range(nb)]
+    tok = np.kron(block_mask, np.ones((b, b), bool))[:n, :n]   # independent expansion
+    out, _ = O.block_sparse_attention(q, k, v, b, lists)
+    np.testing.assert_allclose(out, _sdpa(q, k, v, mask=tok), atol=1e-13)
+
+
+def test_attention_constant_values():
+    n, b, d = 80, 16, 4
+    q, k = _rand((n, d), 27), _rand((n, d), 28)
+    v = np.tile([[0.5, -1.0, 2.0, 3.0]], (n, 1))
+    lists = [[j for j in range(5) if (i + j) % 2 == 0] for i in range(5)]
+    out, _ = O.block_sparse_attention(q, k, v, b, lists)
+    np.testing.assert_allclose(out, v, atol=1e-14)
+
+
+def test_attention_one_block_is_dense_over_that_block():
+    n, b, d = 90, 16, 8
+    q, k, v = _rand((n, d), 29), _rand((n, d), 30), _rand((n, d), 31)
+    lists = [[3]] * O.num_blocks(n, b)
+    out, _ = O.block_sparse_attention(q, k, v, b, lists)
+    np.testing.assert_allclose(out, _sdpa(q, k[48:64], v[48:64]), atol=1e-13)
+    lists = [[5]] * O.num_blocks(n, b)                      # the ragged block
+    out, _ = O.block_sparse_attention(q, k, v, b, lists)
+    np.testing.assert_allclose(out, _sdpa(q, k[80:90], v[80:90]), atol=1e-13)
+
+
+def test_attention_empty_list():
+    q = k = v = _rand((32, 4), 32)
+    out, lse = O.block_sparse_attention(q, k, v, 16, [[], [0]])
+    assert (out[:16] == 0).all() and np.isneginf(lse[:16]).all()
+    assert np.isfinite(lse[16:]).all()
+
+
+# ---------------------------------------------------------------- drift
+
+def test_drift_identical_is_zero():
+    q, k = _rand((3, 20, 4), 33), _rand((3, 20, 4), 34)
+    assert (O.drift(q, k, q, k) == 0).all()
+
+
+@pytest.mark.parametrize("eps", [0.01, -0.03, 0.5])
+def test_drift_uniform_scaling_is_eps(eps):
+    q, k = _rand((2, 30, 4), 35), _rand((2, 30, 4), 36)
+    np.testing.assert_allclose(O.drift((1 + eps) * q, (1 + eps) * k, q, k), abs(eps), rtol=1e-12)
+
+
+def test_drift_closed_form_single_entry():
+    q_ref, k_ref = np.ones((1, 10, 2)), np.ones((1, 10, 2))
+    q = q_ref.copy()
+    q[0, 3, 1] += 0.6
+    np.testing.assert_allclose(O.drift(q, k_ref, q_ref, k_ref), [0.6 / math.sqrt(40.0)], rtol=1e-14)
+
+
+def test_drift_zero_reference():
+    z = np.zeros((2, 4, 2))
+    q = z.copy()
+    q[1, 0, 0] = 1.0
+    d = O.drift(q, z, z, z)
+    assert d[0] == 0 and np.isinf(d[1])
+
+
+def test_refresh_only_perturbed_head_and_strict_threshold():
+    q, k = _rand((4, 50, 8), 37), _rand((4, 50, 8), 38)
+    q2 = q.copy()
+    q2[2] += 0.5 * _rand((50, 8), 39)
+    d = O.drift(q2, k, q, k)
+    assert list(O.refresh_decision(d, 0.05)) == [0, 0, 1, 0]
+    tau = float(np.float32(0.25))
+    assert list(O.refresh_decision([tau], tau)) == [0]          # "exceeds": strict
+
+
+# ---------------------------------------------------------------- trajectory
+
+def _walk(h, n, d, steps, sd, seed):
+    rng = np.random.default_rng(seed)
+    q, k = rng.standard_normal((h, n, d)), rng.standard_normal((h, n, d))
+    out = []
+    for _ in range(steps):
+        out.append((q.copy(), k.copy()))
+        q = q + sd * rng.standard_normal(q.shape)
+        k = k + sd * rng.standard_normal(k.shape)
+    return out
+
+
+def test_trajectory_infinite_threshold_reuses_step0():
+    steps = _walk(2, 64, 8, 5, 0.2, 40)
+    res = list(O.cache_trajectory(steps, 16, [0.8, 0.6], np.inf))
+    for s, (refresh, _, lists, _, _) in enumerate(res):
+        assert refresh.all() if s == 0 else not refresh.any()
+        assert lists == res[0][2]
+
+
+def test_trajectory_zero_threshold_recomputes_every_step():
+    steps = _walk(2, 64, 8, 4, 0.2, 41)
+    res = list(O.cache_trajectory(steps, 16, [0.8, 0.6], 0.0))
+    for (q, k), (refresh, _, lists, counts, scores) in zip(steps, res):
+        assert refresh.all()
+        fresh = O.score_blocks(q, k, 16)
+        np.testing.assert_allclose(scores, fresh, atol=0)
+        _, c2, l2 = O.select_topp(fresh, [0.8, 0.6])
+        assert (counts == c2).all()
+        assert [[list(r) for r in h] for h in lists] == [[list(r) for r in h] for h in l2]
+
+
+def test_trajectory_drift_is_against_last_refresh_snapshot():
+    steps = _walk(1, 64, 8, 6, 0.05, 42)
+    res = list(O.cache_trajectory(steps, 16, [0.9], 0.08))
+    snap = steps[0]
+    for s in range(1, len(steps)):
+        refresh, d, _, _, _ = res[s]
+        want = O.drift(steps[s][0], steps[s][1], snap[0], snap[1])
+        np.testing.assert_allclose(d, want, rtol=1e-14)
+        if refresh[0]:
+            snap = steps[s]
+
+
+def test_turbo_decaying_p_is_nested_and_density_non_increasing():
+    s = np.random.default_rng(43).dirichlet(np.full(30, 0.4), size=(2, 30))
+    stages = O.turbo_schedule(s, [0.95, 0.9, 0.8, 0.6])
+    for (m_prev, c_prev), (m, c) in zip(stages, stages[1:]):
+        assert (m <= m_prev).all()
+        assert (O.density(c, 30) <= O.density(c_prev, 30)).all()
