@@ -1,0 +1,194 @@
+"""Thin ctypes binding of librsa (include/rsa.h): argument marshalling only.
+
+Every step of the path runs in the library's HIP kernels.  torch supplies
+device memory and the current stream; no torch operator touches the data
+here (outputs are only allocated with ``torch.empty``/``torch.zeros``).
+If the library has not been built the first call raises ``RsaLibraryMissing``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "lib", "librsa.so")
+HEADER = os.path.join(os.path.dirname(_PKG), "include", "rsa.h")
+
+RSA_BF16, RSA_FP32 = 0, 1
+OP_SCORE, OP_SELECT, OP_DRIFT, OP_ATTN = 0, 1, 2, 3
+
+
+class RsaLibraryMissing(RuntimeError):
+    pass
+
+
+class RsaError(RuntimeError):
+    def __init__(self, status: int, name: str, call: str):
+        super().__init__(f"{call} failed: {name} ({status})")
+        self.status = status
+        self.name = name
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [
+        ("heads", ctypes.c_int32),
+        ("tokens", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("grid_f", ctypes.c_int32),
+        ("grid_h", ctypes.c_int32),
+        ("grid_w", ctypes.c_int32),
+        ("block", ctypes.c_int32),
+        ("dtype", ctypes.c_int32),
+        ("softmax_scale", ctypes.c_float),
+    ]
+
+    @property
+    def nblocks(self) -> int:
+        return -(-self.tokens // self.block)
+
+    def __repr__(self):
+        return ("Problem(heads=%d, tokens=%d, head_dim=%d, grid=(%d,%d,%d), block=%d, dtype=%d, scale=%g)"
+                % (self.heads, self.tokens, self.head_dim, self.grid_f, self.grid_h, self.grid_w,
+                   self.block, self.dtype, self.softmax_scale))
+
+
+_P = ctypes.c_void_p
+_lib = None
+
+
+def _declare(lib):
+    pp = ctypes.POINTER(Problem)
+    sz, i32, f32 = ctypes.c_size_t, ctypes.c_int32, ctypes.c_float
+    sigs = {
+        "rsa_workspace_bytes": (sz, [pp, i32]),
+        "rsa_status_str": (ctypes.c_char_p, [i32]),
+        "rsa_version": (i32, []),
+        "rsa_score_blocks": (i32, [pp, _P, _P, _P, _P, _P, sz, _P]),
+        "rsa_select_topp": (i32, [pp, _P, _P, i32, _P, _P, _P, _P, _P, _P, sz, _P]),
+        "rsa_mask_drift": (i32, [pp, _P, _P, _P, _P, f32, i32, _P, _P, _P, sz, _P]),
+        "rsa_block_sparse_attn": (i32, [pp, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
+    }
+    for name, (res, args) in sigs.items():
+        fn = getattr(lib, name)
+        fn.restype = res
+        fn.argtypes = args
+    return lib
+
+
+def lib():
+    """The loaded librsa (raises RsaLibraryMissing when it is not built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RsaLibraryMissing(
+                f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; g.build()'`")
+        _lib = _declare(ctypes.CDLL(LIB_PATH))
+    return _lib
+
+
+def declared_functions(header: str = HEADER):
+    """Names of the functions include/rsa.h declares."""
+    text = open(header).read()
+    return sorted(set(re.findall(r"^\s*(?:[A-Za-z_][\w\s\*]*?)\b(rsa_\w+)\s*\(", text, re.M)))
+
+
+def _check(status: int, call: str):
+    if status != 0:
+        raise RsaError(status, lib().rsa_status_str(status).decode(), call)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dtype_code(dt: torch.dtype) -> int:
+    if dt == torch.bfloat16:
+        return RSA_BF16
+    if dt == torch.float32:
+        return RSA_FP32
+    raise TypeError(f"unsupported dtype {dt}: q/k/v must be bfloat16 or float32")
+
+
+def make_problem(q: torch.Tensor, grid, block: int, softmax_scale: float = 0.0) -> Problem:
+    """Descriptor for q/k/v of shape [heads, tokens, head_dim] on a (F, H, W) grid."""
+    h, n, d = q.shape
+    f, y, x = grid
+    return Problem(h, n, d, f, y, x, block, _dtype_code(q.dtype), float(softmax_scale))
+
+
+def workspace_bytes(p: Problem, op: int) -> int:
+    return int(lib().rsa_workspace_bytes(ctypes.byref(p), op))
+
+
+def _workspace(p: Problem, op: int, device, ws: Optional[torch.Tensor]):
+    need = workspace_bytes(p, op)
+    if need == 0:
+        return None, 0
+    if ws is None:
+        ws = torch.empty(need, dtype=torch.uint8, device=device)
+    return ws, ws.numel() * ws.element_size()
+
+
+def score_blocks(q, k, p: Problem, head_active=None, out=None, workspace=None):
+    """PARK block scores [heads, NB, NB] fp32 (rsa_score_blocks)."""
+    nb = p.nblocks
+    if out is None:
+        out = torch.empty((p.heads, nb, nb), dtype=torch.float32, device=q.device)
+    ws, wsb = _workspace(p, OP_SCORE, q.device, workspace)
+    _check(lib().rsa_score_blocks(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(head_active), _ptr(out),
+                                  _ptr(ws), wsb, _stream(q)), "rsa_score_blocks")
+    return out
+
+
+def select_topp(scores, top_p, p: Problem, max_blocks: int = 0, head_active=None, mask=None,
+                counts=None, block_idx=None, density=None, want_density: bool = True):
+    """Top-p selection -> (mask u8, counts i32, block_idx i32, density fp32 or None)."""
+    nb = p.nblocks
+    dev = scores.device
+    if mask is None:
+        mask = torch.zeros((p.heads, nb, nb), dtype=torch.uint8, device=dev)
+    if counts is None:
+        counts = torch.zeros((p.heads, nb), dtype=torch.int32, device=dev)
+    if block_idx is None:
+        block_idx = torch.zeros((p.heads, nb, nb), dtype=torch.int32, device=dev)
+    if density is None and want_density:
+        density = torch.zeros((p.heads,), dtype=torch.float32, device=dev)
+    _check(lib().rsa_select_topp(ctypes.byref(p), _ptr(scores), _ptr(top_p), int(max_blocks),
+                                 _ptr(head_active), _ptr(mask), _ptr(counts), _ptr(block_idx),
+                                 _ptr(density), None, 0, _stream(scores)), "rsa_select_topp")
+    return mask, counts, block_idx, density
+
+
+def mask_drift(q, k, q_ref, k_ref, p: Problem, threshold: float, update_ref: bool = True,
+               drift=None, refresh=None, workspace=None):
+    """Per-head drift and refresh flags -> (drift fp32 [H], refresh u8 [H])."""
+    if drift is None:
+        drift = torch.empty((p.heads,), dtype=torch.float32, device=q.device)
+    if refresh is None:
+        refresh = torch.empty((p.heads,), dtype=torch.uint8, device=q.device)
+    ws, wsb = _workspace(p, OP_DRIFT, q.device, workspace)
+    _check(lib().rsa_mask_drift(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(q_ref), _ptr(k_ref),
+                                float(threshold), int(bool(update_ref)), _ptr(drift), _ptr(refresh),
+                                _ptr(ws), wsb, _stream(q)), "rsa_mask_drift")
+    return drift, refresh
+
+
+def block_sparse_attn(q, k, v, counts, block_idx, p: Problem, out=None, lse=None,
+                      want_lse: bool = True):
+    """Attention over the listed key blocks -> (out like q, lse fp32 [H, N] or None)."""
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((p.heads, p.tokens), dtype=torch.float32, device=q.device)
+    _check(lib().rsa_block_sparse_attn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(counts),
+                                       _ptr(block_idx), _ptr(out), _ptr(lse), None, 0, _stream(q)),
+           "rsa_block_sparse_attn")
+    return out, lse

@@ -1,0 +1,66 @@
+"""Cross-step mask reuse: a host loop over the four library calls.
+
+RAPID (Reusing Attention Sparsity with Inter-step Adaptation for Efficient
+Video Diffusion), Abstract: estimate block importance once, cache the scores
+and the mask, reuse them in later denoising steps; the cached scores also
+allow a multi-stage re-pruning (Turbo mode).  HEART (Exploiting Head
+Heterogeneity in Sparse Attention for Video Diffusion), Abstract: per head,
+refresh the cached mask only when its query-key drift exceeds a threshold.
+
+All state lives in device buffers owned by this object; every step enqueues
+the library calls on the current stream and never synchronises.  The refresh
+flags stay on the device and gate the scoring and selection kernels.
+"""
+from __future__ import annotations
+
+import torch
+
+from . import binding as B
+
+
+class MaskCache:
+    def __init__(self, problem: B.Problem, top_p: torch.Tensor, threshold: float,
+                 max_blocks: int = 0, device=None):
+        p = problem
+        dev = device if device is not None else top_p.device
+        nb = p.nblocks
+        dt = torch.bfloat16 if p.dtype == B.RSA_BF16 else torch.float32
+        self.p = p
+        self.top_p = top_p
+        self.threshold = float(threshold)
+        self.max_blocks = int(max_blocks)
+        self.scores = torch.zeros((p.heads, nb, nb), dtype=torch.float32, device=dev)
+        self.mask = torch.zeros((p.heads, nb, nb), dtype=torch.uint8, device=dev)
+        self.counts = torch.zeros((p.heads, nb), dtype=torch.int32, device=dev)
+        self.block_idx = torch.zeros((p.heads, nb, nb), dtype=torch.int32, device=dev)
+        self.density = torch.zeros((p.heads,), dtype=torch.float32, device=dev)
+        self.q_ref = torch.zeros((p.heads, p.tokens, p.head_dim), dtype=dt, device=dev)
+        self.k_ref = torch.zeros_like(self.q_ref)
+        self.drift = torch.zeros((p.heads,), dtype=torch.float32, device=dev)
+        self.refresh = torch.zeros((p.heads,), dtype=torch.uint8, device=dev)
+        self.score_ws = torch.empty(max(1, B.workspace_bytes(p, B.OP_SCORE)), dtype=torch.uint8, device=dev)
+        self.drift_ws = torch.empty(max(1, B.workspace_bytes(p, B.OP_DRIFT)), dtype=torch.uint8, device=dev)
+        self.steps = 0
+
+    def update_mask(self, q: torch.Tensor, k: torch.Tensor):
+        """Drift check, then re-score / re-select the refreshed heads (all at step 0)."""
+        B.mask_drift(q, k, self.q_ref, self.k_ref, self.p, self.threshold, update_ref=True,
+                     drift=self.drift, refresh=self.refresh, workspace=self.drift_ws)
+        active = None if self.steps == 0 else self.refresh
+        B.score_blocks(q, k, self.p, head_active=active, out=self.scores, workspace=self.score_ws)
+        B.select_topp(self.scores, self.top_p, self.p, self.max_blocks, head_active=active,
+                      mask=self.mask, counts=self.counts, block_idx=self.block_idx,
+                      density=self.density)
+        self.steps += 1
+
+    def step(self, q, k, v, out=None, lse=None):
+        """One denoising step's attention with the cached (or refreshed) mask."""
+        self.update_mask(q, k)
+        return B.block_sparse_attn(q, k, v, self.counts, self.block_idx, self.p, out=out, lse=lse)
+
+    def turbo(self, top_p: torch.Tensor, max_blocks: int | None = None):
+        """RAPID Turbo mode: re-select every head on the cached scores (no re-scoring)."""
+        self.top_p = top_p
+        B.select_topp(self.scores, top_p, self.p, self.max_blocks if max_blocks is None else max_blocks,
+                      mask=self.mask, counts=self.counts, block_idx=self.block_idx,
+                      density=self.density)

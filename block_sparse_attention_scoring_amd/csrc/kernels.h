@@ -1,0 +1,46 @@
+// Internal interface between the C-ABI layer (api.hip) and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace rsa {
+
+// Validated problem, derived sizes included.
+struct Problem {
+  int heads, tokens, head_dim, block, nb;
+  int dtype;    // 0 = bf16, 1 = fp32
+  float scale;  // logit scale actually used
+};
+
+// Scoring workspace: pooled keys (fp32, already times scale*log2 e), per
+// block max |.|, their 2-term fp16 split (rows padded to a multiple of 32
+// with zeros) and the per-head power-of-two unscale factor.
+struct ScoreWs {
+  float* kt;
+  float* bmax;
+  _Float16* khi;
+  _Float16* klo;
+  float* inv_t;
+};
+constexpr int kScoreRowPad = 32;
+size_t score_ws_layout(const Problem& p, ScoreWs* ws, void* base);
+
+constexpr int kDriftGroups = 64;  // partial sums per head
+size_t drift_ws_bytes(const Problem& p);
+
+hipError_t launch_scoring(const Problem& p, const void* q, const void* k,
+                          const uint8_t* head_active, float* scores, const ScoreWs& ws,
+                          hipStream_t stream);
+hipError_t launch_select(const Problem& p, const float* scores, const float* top_p,
+                         int max_blocks, const uint8_t* head_active, uint8_t* mask,
+                         int32_t* counts, int32_t* idx, float* density, hipStream_t stream);
+hipError_t launch_drift(const Problem& p, const void* q, const void* k, void* q_ref,
+                        void* k_ref, float threshold, int update_ref, float* drift,
+                        uint8_t* refresh, void* ws, hipStream_t stream);
+hipError_t launch_attention(const Problem& p, const void* q, const void* k, const void* v,
+                            const int* counts, const int* idx, void* out, float* lse,
+                            hipStream_t stream);
+
+}  // namespace rsa

@@ -1,0 +1,215 @@
+/*
+ * librsa - block-sparse attention scoring for video diffusion transformers,
+ * hand-written HIP kernels for gfx950 (MI355X).
+ *
+ * Four calls make the hot path.  Each is defined by the pages it cites:
+ *
+ *   rsa_score_blocks      PARK's block scorer (PARK: Accurate Block Retrieval
+ *                         for Sparse Attention in Video Diffusion Transformers,
+ *                         Abstract): pool each key block to its mean, take a
+ *                         softmax of every query over the pooled key blocks,
+ *                         average those distributions within each query block.
+ *   rsa_select_topp       online top-p block selection with a per-head
+ *                         threshold (HASTE: Training-Free Video Diffusion
+ *                         Acceleration via Head-Wise Adaptive Sparse
+ *                         Attention, Abstract; HEART: Exploiting Head
+ *                         Heterogeneity in Sparse Attention for Video
+ *                         Diffusion, Abstract).
+ *   rsa_mask_drift        Temporal Mask Reuse's per-head query-key drift
+ *                         signal and refresh decision (HEART, Abstract; HASTE,
+ *                         Abstract); with RAPID (Reusing Attention Sparsity
+ *                         with Inter-step Adaptation for Efficient Video
+ *                         Diffusion, Abstract) it lets cached scores and masks
+ *                         be reused across denoising steps.
+ *   rsa_block_sparse_attn attention computed only inside the retrieved key
+ *                         blocks (PARK, Abstract).
+ *
+ * Common conventions
+ * ------------------
+ * Tensors q, k, v, out are [heads, tokens, head_dim], row-major, tokens in
+ * (frame, height, width) raster order.  A block is a run of `block`
+ * consecutive tokens; query blocks and key blocks share one partition of
+ * NB = ceil(tokens / block) blocks and the last block may be shorter.
+ *
+ * Pointers are device pointers (HBM) unless a comment says "host".  The
+ * caller owns every buffer, including the workspace; the library never
+ * allocates, frees or keeps a device pointer and holds no global state, so
+ * calls on different streams do not interfere.  Every call only enqueues
+ * kernels on `stream` and returns without synchronising.
+ *
+ * Errors: arguments are validated on the host before anything is enqueued;
+ * on any error nothing is launched and no output is touched.  The status is
+ * the return value; nothing is printed, nothing aborts and no exception
+ * crosses the ABI.  A launch failure reported by the HIP runtime returns
+ * RSA_ERR_HIP; device faults surface at the caller's next synchronisation.
+ *
+ * Results are bitwise deterministic for identical inputs (fixed reduction
+ * orders; no floating-point atomics).
+ */
+#ifndef RSA_H
+#define RSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define RSA_VERSION 10000 /* 1.0.0 */
+
+/* Element type of q, k, v, the drift snapshots and the attention output. */
+typedef enum { RSA_BF16 = 0, RSA_FP32 = 1 } rsa_dtype;
+
+typedef enum {
+  RSA_OK = 0,
+  RSA_ERR_NULL = 1,      /* a required pointer is NULL */
+  RSA_ERR_SHAPE = 2,     /* sizes out of range or inconsistent */
+  RSA_ERR_DTYPE = 3,     /* unknown dtype */
+  RSA_ERR_ALIGN = 4,     /* a pointer is not 16-byte aligned */
+  RSA_ERR_WORKSPACE = 5, /* workspace missing, too small or not 256-byte aligned */
+  RSA_ERR_HIP = 6,       /* the HIP runtime rejected a launch */
+  RSA_ERR_ARG = 7        /* a scalar argument is out of range (e.g. NaN threshold) */
+} rsa_status;
+
+typedef enum { RSA_OP_SCORE = 0, RSA_OP_SELECT = 1, RSA_OP_DRIFT = 2, RSA_OP_ATTN = 3 } rsa_op;
+
+/*
+ * Problem descriptor (host struct, read during the call only).
+ *   heads >= 1; tokens == grid_f * grid_h * grid_w (each >= 1);
+ *   head_dim in {64, 128}; block in {64, 128}; NB = ceil(tokens/block) <= 4096;
+ *   dtype: rsa_dtype;
+ *   softmax_scale: logit scale shared by scoring and attention; a value <= 0
+ *   (or NaN) means 1/sqrt(head_dim); +inf is rejected (RSA_ERR_ARG).
+ */
+typedef struct {
+  int32_t heads;
+  int32_t tokens;
+  int32_t head_dim;
+  int32_t grid_f;
+  int32_t grid_h;
+  int32_t grid_w;
+  int32_t block;
+  int32_t dtype;
+  float softmax_scale;
+} rsa_problem;
+
+/*
+ * Bytes of workspace `op` needs for `p` (0 when none).  Returns 0 for an
+ * invalid problem as well; the compute calls report that case themselves.
+ */
+size_t rsa_workspace_bytes(const rsa_problem* p, int32_t op);
+
+/* Static string naming a status code ("RSA_OK", ...); "unknown" otherwise. */
+const char* rsa_status_str(int32_t status);
+
+/* RSA_VERSION of the built library. */
+int32_t rsa_version(void);
+
+/*
+ * PARK block scores (PARK, Abstract; the Summary calls it keeping each
+ * query's own information).
+ *
+ *   For head h, key block J with b_J tokens:  Kbar[h,J] = mean of its keys.
+ *   For query i:  P[i,J] = softmax over J of  scale * <q_i, Kbar[h,J]>.
+ *   For query block I with b_I queries:  scores[h,I,J] = mean over i in I of P[i,J].
+ *
+ * q, k: [heads, tokens, head_dim] of `dtype`, 16-byte aligned.
+ * head_active: [heads] u8 or NULL (= all heads).  Heads with 0 are skipped and
+ *   their rows of `scores` are left as they are (a cached mask's scores).
+ * scores: [heads, NB, NB] fp32 output; every row sums to 1 up to rounding.
+ * ws / ws_bytes: workspace of at least rsa_workspace_bytes(p, RSA_OP_SCORE)
+ *   bytes, 256-byte aligned; its contents on entry do not matter.
+ * Logits are formed to about fp32 accuracy (a 2-term fp16 split of the pooled
+ * keys on the matrix cores), the softmax and the query-block means in fp32.
+ */
+rsa_status rsa_score_blocks(const rsa_problem* p, const void* q, const void* k,
+                            const uint8_t* head_active, float* scores,
+                            void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Top-p block selection (HASTE, Abstract: online top-p; HEART, Abstract:
+ * one threshold per head under a global sparsity budget).
+ *
+ *   Row (h,I): key blocks ordered by score descending, equal scores by index
+ *   ascending; running mass in fp64; keep the smallest prefix whose mass is
+ *   >= top_p[h] (at least one block; top_p[h] >= 1 keeps all NB; no prefix
+ *   reaching top_p[h], e.g. NaN, keeps all NB); then at most max_blocks
+ *   blocks when max_blocks > 0.
+ *
+ * scores: [heads, NB, NB] fp32 (any non-negative values; rows need not sum to 1).
+ * top_p: [heads] fp32 thresholds (device).
+ * max_blocks: >= 0; 0 = no per-row cap.
+ * head_active: [heads] u8 or NULL; rows of inactive heads are left untouched.
+ * mask: [heads, NB, NB] u8 output, 1 = block kept.
+ * counts: [heads, NB] int32 output, blocks kept per row.
+ * block_idx: [heads, NB, NB] int32 output; row (h,I) lists its kept key
+ *   blocks in ascending order in its first counts[h,I] entries; the other
+ *   entries of the row are not written.
+ * density: [heads] fp32 output or NULL: kept pairs / NB^2 per head, recomputed
+ *   from all rows of `counts` (cached rows of inactive heads included).
+ * ws / ws_bytes: unused (rsa_workspace_bytes returns 0); may be NULL / 0.
+ */
+rsa_status rsa_select_topp(const rsa_problem* p, const float* scores, const float* top_p,
+                           int32_t max_blocks, const uint8_t* head_active,
+                           uint8_t* mask, int32_t* counts, int32_t* block_idx,
+                           float* density, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Per-head query-key drift and refresh flags (HEART, Abstract: refresh a
+ * cached mask only when the head's drift exceeds a prescribed threshold;
+ * HASTE, Abstract: skip mask prediction from query-key drift).
+ *
+ *   drift[h] = sqrt(|Q_h - Qref_h|^2 + |K_h - Kref_h|^2) / sqrt(|Qref_h|^2 + |Kref_h|^2)
+ *   refresh[h] = drift[h] > threshold  (strict; an all-zero snapshot gives
+ *   drift 0 if nothing changed and +inf otherwise)
+ *
+ * Sums of squares are accumulated in fp64 in a fixed order; the comparison is
+ * done in fp64 before drift is rounded to fp32.
+ * q, k: current [heads, tokens, head_dim] of `dtype`.
+ * q_ref, k_ref: snapshots, same shape and dtype.  When update_ref != 0 the
+ *   snapshot of every refreshed head is overwritten with its current q, k
+ *   (after the drift is measured), so the next call measures against the
+ *   step at which that head's mask was recomputed.
+ * threshold: finite or +inf; NaN is rejected (RSA_ERR_ARG).
+ * drift: [heads] fp32 output; refresh: [heads] u8 output (pass it as
+ *   head_active to rsa_score_blocks / rsa_select_topp).
+ * ws / ws_bytes: at least rsa_workspace_bytes(p, RSA_OP_DRIFT), 256-byte aligned.
+ */
+rsa_status rsa_mask_drift(const rsa_problem* p, const void* q, const void* k,
+                          void* q_ref, void* k_ref, float threshold, int32_t update_ref,
+                          float* drift, uint8_t* refresh,
+                          void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Block-sparse attention (PARK, Abstract: attention computed only inside the
+ * retrieved blocks).  For query i of block I of head h, the visible keys are
+ * the tokens of the key blocks block_idx[h,I,0..counts[h,I]); the softmax is
+ * normalised over those keys only:
+ *
+ *   out[h,i,:] = sum_t softmax_t(scale * <q_i, k_t>) v_t,
+ *   lse[h,i]   = log sum_t exp(scale * <q_i, k_t>)   (natural log).
+ *
+ * q, k, v: [heads, tokens, head_dim] of `dtype`, 16-byte aligned.
+ * counts: [heads, NB] int32, each in [0, NB]; block_idx: [heads, NB, NB]
+ *   int32, entries in [0, NB) (e.g. the output of rsa_select_topp, fresh or
+ *   cached).  A row with count 0 gives out = 0 and lse = -inf.
+ * out: [heads, tokens, head_dim] of `dtype` (bf16 rounded to nearest even).
+ * lse: [heads, tokens] fp32 output or NULL.
+ * bf16 inputs: bf16 matrix-core products with fp32 accumulation and an fp32
+ *   online softmax; fp32 inputs: fp32 arithmetic throughout.
+ * ws / ws_bytes: unused (rsa_workspace_bytes returns 0); may be NULL / 0.
+ * Out-of-range counts or indices are not checked on the device: the caller
+ * guarantees them (rsa_select_topp's outputs always satisfy them).
+ */
+rsa_status rsa_block_sparse_attn(const rsa_problem* p, const void* q, const void* k,
+                                 const void* v, const int32_t* counts,
+                                 const int32_t* block_idx, void* out, float* lse,
+                                 void* ws, size_t ws_bytes, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RSA_H */
