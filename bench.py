@@ -1,0 +1,263 @@
+#!/usr/bin/env python3
+"""Benchmark of the block-sparse attention scoring hot path on one MI355X.
+
+One step is one pass of the whole path over one layer's q/k/v of the
+Wan2.1-14B-like 720p shape (40 heads, 21x45x80 = 75,600 tokens, head_dim 128,
+block 128, top-p 0.9), inputs resident in HBM:
+
+  rsa_mask_drift (drift of every head against its snapshot, snapshot update of
+  refreshed heads) -> rsa_score_blocks (every head re-scored: a fresh-mask
+  step, the most expensive step of a reuse trajectory) -> rsa_select_topp ->
+  rsa_block_sparse_attn.
+
+Reported value: effective TFLOP/s of the step = executed attention FLOPs
+(4 * b_I * b_J * head_dim summed over the selected (query block, key block)
+pairs) / step time.  The attention call alone (ms per call, effective
+TFLOP/s) and every other kernel's time are reported beside it, each averaged
+over the timed steps with HIP events recorded on the stream the library
+launches on.  The oracle (fp64 NumPy) is timed on a bounded sample on the
+host cores as a CPU baseline.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 matrix-core peak
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak
+WORKLOAD = "wan14b_720p"
+ATTN_PROFILE = os.path.join(ROOT, "profiles", "attn_bf16_wan14b_720p_pmc.txt")
+ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_scoring_amd", "csrc", "attn.hip")
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (HBM counter calibration)")
+    return ap.parse_args()
+
+
+def source_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def profiled_traffic():
+    """HBM bytes per attention launch from the committed PMC summary, if current."""
+    if not os.path.exists(ATTN_PROFILE):
+        return None
+    text = open(ATTN_PROFILE).read()
+    m_hash = re.search(r"attn\.hip sha256\[:16\]: (\w+)", text)
+    m_bytes = re.search(r"hbm_bytes_per_launch: ([0-9.eE+]+)", text)
+    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(ATTN_SOURCE):
+        return None
+    return float(m_bytes.group(1))
+
+
+def executed_flops(counts, idx, wl):
+    import numpy as np
+    nb, b, n, d = wl.nblocks, wl.block, wl.tokens, wl.head_dim
+    bsz = np.full(nb, b, np.int64)
+    bsz[-1] = n - b * (nb - 1)
+    keep = np.arange(nb)[None, None, :] < counts[..., None]
+    key_tokens = np.where(keep, bsz[np.clip(idx, 0, nb - 1)], 0).sum(-1)     # [H, NB]
+    return float(4 * d * (key_tokens * bsz[None, :]).sum())
+
+
+def cpu_baseline(inp, wl, counts_gpu, idx_gpu, total_flops):
+    """Oracle on a bounded sample: head 0 scored + selected in full, attention on
+    24 evenly spaced query blocks of head 0 (the GPU's lists); extrapolated to
+    the whole step by head count (scoring) and executed FLOPs (attention)."""
+    import numpy as np
+    import oracle as O
+    import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    q0, k0, v0 = W.to_f64(inp.q[0]), W.to_f64(inp.k[0]), W.to_f64(inp.v[0])
+    scale = 1.0 / np.sqrt(wl.head_dim)
+    t0 = time.perf_counter()
+    s = O.score_head(q0, k0, wl.block, scale)
+    for i in range(wl.nblocks):
+        O.select_row(s[i], float(inp.top_p[0]))
+    t_ss = time.perf_counter() - t0
+    rows = np.linspace(0, wl.nblocks - 1, 24).astype(int)
+    lists = [idx_gpu[0, i, :counts_gpu[0, i]] for i in range(wl.nblocks)]
+    t0 = time.perf_counter()
+    O.block_sparse_attention(q0, k0, v0, wl.block, lists, scale, query_blocks=list(rows))
+    t_at = time.perf_counter() - t0
+    nb, b, n = wl.nblocks, wl.block, wl.tokens
+    bsz = np.full(nb, b, np.int64)
+    bsz[-1] = n - b * (nb - 1)
+    sample_flops = float(sum(4 * wl.head_dim * bsz[i] * bsz[lists[i]].sum() for i in rows))
+    t_step = wl.heads * t_ss + t_at * total_flops / sample_flops
+    return {
+        "value": round(total_flops / t_step / 1e12, 6),
+        "unit": "TFLOP/s",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"fp64 oracle: head 0 of {wl.name} scored and top-p selected in full "
+                   f"({t_ss:.1f} s, x{wl.heads} heads) + attention on 24 of {nb} query blocks "
+                   f"of head 0 ({t_at:.1f} s, scaled by executed FLOPs); "
+                   f"extrapolated step {t_step:.0f} s"),
+        "ms_per_step": round(t_step * 1e3, 1),
+    }
+
+
+def copy_probe(mib):
+    import torch
+    n = mib * (1 << 20)
+    a = torch.empty(n, dtype=torch.uint8, device="cuda:0").fill_(1)
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes": n, "launches": 3}))
+
+
+def main():
+    args = parse()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on exactly one GPU: the four kernels work per head with no "
+              "exchange between GPUs, so a multi-GPU run is not provided (see DESIGN.md "
+              "for how heads would shard).", file=sys.stderr)
+        sys.exit(2)
+    if args.copy_probe:
+        copy_probe(args.copy_probe)
+        return
+
+    import numpy as np
+    import torch
+    import workloads as W
+    import block_sparse_attention_scoring_amd as R
+
+    wl = W.CONFIGS[args.workload]
+    t_gen = time.perf_counter()
+    inp = W.make_inputs(wl)
+    t_gen = time.perf_counter() - t_gen
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
+    p = R.make_problem(q, wl.grid, wl.block)
+    nb = wl.nblocks
+    top_p = torch.from_numpy(inp.top_p).to(dev)
+    q_ref, k_ref = q.clone(), k.clone()
+    scores = torch.empty((wl.heads, nb, nb), dtype=torch.float32, device=dev)
+    mask = torch.empty((wl.heads, nb, nb), dtype=torch.uint8, device=dev)
+    counts = torch.empty((wl.heads, nb), dtype=torch.int32, device=dev)
+    idx = torch.empty((wl.heads, nb, nb), dtype=torch.int32, device=dev)
+    density = torch.empty((wl.heads,), dtype=torch.float32, device=dev)
+    drift = torch.empty((wl.heads,), dtype=torch.float32, device=dev)
+    refresh = torch.empty((wl.heads,), dtype=torch.uint8, device=dev)
+    out = torch.empty_like(q)
+    lse = torch.empty((wl.heads, wl.tokens), dtype=torch.float32, device=dev)
+    ws_s = torch.empty(R.workspace_bytes(p, R.OP_SCORE), dtype=torch.uint8, device=dev)
+    ws_d = torch.empty(R.workspace_bytes(p, R.OP_DRIFT), dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)   # the library launches on this stream
+
+    names = ("drift", "score", "select", "attn")
+    calls = (
+        lambda: R.mask_drift(q, k, q_ref, k_ref, p, wl.drift_threshold, update_ref=True,
+                             drift=drift, refresh=refresh, workspace=ws_d),
+        lambda: R.score_blocks(q, k, p, out=scores, workspace=ws_s),
+        lambda: R.select_topp(scores, top_p, p, mask=mask, counts=counts, block_idx=idx,
+                              density=density),
+        lambda: R.block_sparse_attn(q, k, v, counts, idx, p, out=out, lse=lse),
+    )
+
+    def step(events=None):
+        for j, fn in enumerate(calls):
+            if events is not None:
+                events[j][0].record(stream)
+            fn()
+            if events is not None:
+                events[j][1].record(stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in names]
+          for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(ev[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    per = {n: float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)]))
+           for j, n in enumerate(names)}
+    ms_step = wall * 1e3 / args.steps
+
+    c_h, i_h = counts.cpu().numpy(), idx.cpu().numpy()
+    flops = executed_flops(c_h, i_h, wl)
+    dense_flops = 4.0 * wl.tokens * wl.tokens * wl.head_dim * wl.heads
+    dens = density.cpu().numpy()
+    attn_tflops = flops / (per["attn"] * 1e-3) / 1e12
+    # scoring's algorithmic HBM bytes: q and k read once, scores written once
+    esz = 2 if wl.dtype == "bf16" else 4
+    score_bytes = 2.0 * wl.heads * wl.tokens * wl.head_dim * esz + 4.0 * wl.heads * nb * nb
+    drift_bytes = 4.0 * wl.heads * wl.tokens * wl.head_dim * esz
+
+    res = {
+        "metric": "ms per block-sparse attention call + effective TFLOP/s at 720p DiT shape",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded smooth 3-D field + noise, Wan2.1-14B 720p latent shape; no weights)",
+        "config": {
+            "workload": wl.name, "heads": wl.heads, "grid": list(wl.grid), "tokens": wl.tokens,
+            "head_dim": wl.head_dim, "block": wl.block, "top_p": float(inp.top_p[0]),
+            "parallelism": "single GPU",
+        },
+        "attn_ms_per_call": round(per["attn"], 3),
+        "attn_effective_tflops": round(attn_tflops, 1),
+        "attn_dense_equivalent_tflops": round(dense_flops / (per["attn"] * 1e-3) / 1e12, 1),
+        "score_ms": round(per["score"], 3),
+        "select_ms": round(per["select"], 3),
+        "drift_ms": round(per["drift"], 3),
+        "score_hbm_gbs": round(score_bytes / (per["score"] * 1e-3) / 1e9, 1),
+        "score_hbm_frac": round(score_bytes / (per["score"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "drift_hbm_gbs": round(drift_bytes / (per["drift"] * 1e-3) / 1e9, 1),
+        "density_mean": round(float(dens.mean()), 4),
+        "density_min_max": [round(float(dens.min()), 4), round(float(dens.max()), 4)],
+        "executed_tflop_per_step": round(flops / 1e12, 3),
+        "input_generation_s": round(t_gen, 1),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "traffic": profiled_traffic(),
+            "kernel": "attn_bf16_kernel<128,128>",
+        },
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, wl, c_h, i_h, flops)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()
