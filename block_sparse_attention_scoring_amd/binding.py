@@ -182,13 +182,14 @@ def mask_drift(q, k, q_ref, k_ref, p: Problem, threshold: float, update_ref: boo
 
 
 def block_sparse_attn(q, k, v, counts, block_idx, p: Problem, out=None, lse=None,
-                      want_lse: bool = True):
+                      want_lse: bool = True, workspace=None):
     """Attention over the listed key blocks -> (out like q, lse fp32 [H, N] or None)."""
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
         lse = torch.empty((p.heads, p.tokens), dtype=torch.float32, device=q.device)
+    ws, wsb = _workspace(p, OP_ATTN, q.device, workspace)
     _check(lib().rsa_block_sparse_attn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(counts),
-                                       _ptr(block_idx), _ptr(out), _ptr(lse), None, 0, _stream(q)),
-           "rsa_block_sparse_attn")
+                                       _ptr(block_idx), _ptr(out), _ptr(lse), _ptr(ws), wsb,
+                                       _stream(q)), "rsa_block_sparse_attn")
     return out, lse

@@ -40,6 +40,7 @@ class MaskCache:
         self.refresh = torch.zeros((p.heads,), dtype=torch.uint8, device=dev)
         self.score_ws = torch.empty(max(1, B.workspace_bytes(p, B.OP_SCORE)), dtype=torch.uint8, device=dev)
         self.drift_ws = torch.empty(max(1, B.workspace_bytes(p, B.OP_DRIFT)), dtype=torch.uint8, device=dev)
+        self.attn_ws = torch.empty(max(1, B.workspace_bytes(p, B.OP_ATTN)), dtype=torch.uint8, device=dev)
         self.steps = 0
 
     def update_mask(self, q: torch.Tensor, k: torch.Tensor):
@@ -56,7 +57,8 @@ class MaskCache:
     def step(self, q, k, v, out=None, lse=None):
         """One denoising step's attention with the cached (or refreshed) mask."""
         self.update_mask(q, k)
-        return B.block_sparse_attn(q, k, v, self.counts, self.block_idx, self.p, out=out, lse=lse)
+        return B.block_sparse_attn(q, k, v, self.counts, self.block_idx, self.p, out=out, lse=lse,
+                                   workspace=self.attn_ws)
 
     def turbo(self, top_p: torch.Tensor, max_blocks: int | None = None):
         """RAPID Turbo mode: re-select every head on the cached scores (no re-scoring)."""

@@ -44,6 +44,7 @@ size_t ws_bytes_for(const rsa::Problem& p, int op) {
   switch (op) {
     case RSA_OP_SCORE: return rsa::score_ws_layout(p, nullptr, nullptr);
     case RSA_OP_DRIFT: return rsa::drift_ws_bytes(p);
+    case RSA_OP_ATTN: return rsa::attn_ws_bytes(p);
     default: return 0;
   }
 }
@@ -134,8 +135,6 @@ rsa_status rsa_mask_drift(const rsa_problem* p, const void* q, const void* k, vo
 rsa_status rsa_block_sparse_attn(const rsa_problem* p, const void* q, const void* k, const void* v,
                                  const int32_t* counts, const int32_t* block_idx, void* out,
                                  float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
-  (void)ws;
-  (void)ws_bytes;
   rsa::Problem pr;
   rsa_status st = make_problem(p, &pr);
   if (st != RSA_OK) return st;
@@ -143,7 +142,9 @@ rsa_status rsa_block_sparse_attn(const rsa_problem* p, const void* q, const void
       out == nullptr)
     return RSA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return RSA_ERR_ALIGN;
-  return hip_status(rsa::launch_attention(pr, q, k, v, counts, block_idx, out, lse, stream));
+  st = check_ws(pr, RSA_OP_ATTN, ws, ws_bytes);
+  if (st != RSA_OK) return st;
+  return hip_status(rsa::launch_attention(pr, q, k, v, counts, block_idx, out, lse, ws, stream));
 }
 
 }  // extern "C"

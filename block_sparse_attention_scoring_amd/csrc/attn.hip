@@ -23,7 +23,26 @@
 namespace rsa {
 namespace {
 
-template <int D, int B>
+typedef __attribute__((address_space(1))) void gvoid;
+typedef __attribute__((address_space(3))) void lvoid;
+
+// Position of `key` inside its 16-key group of V^T: the S^T result layout
+// gives lane half h keys {4h..4h+3, 8+4h..8+4h+3}, so groups 1 and 2 of
+// four keys are swapped.
+__host__ __device__ __forceinline__ int vt_pos(int key) {
+  const int g4 = (key >> 2) & 3;
+  const int sw = ((g4 & 1) << 1) | (g4 >> 1);
+  return (key & ~15) | (sw << 2) | (key & 3);
+}
+
+// XOR swizzle of the 16-byte chunks of an LDS tile row holding `cpr` chunks:
+// 16 consecutive rows read at one logical chunk hit 16 distinct bank groups.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  return CPR == 16 ? (r & 15) : ((r >> 1) & 7);
+}
+
+template <int D, int B, int NBUF>
 struct AttnShape {
   static constexpr int kWaves = B / 32;
   static constexpr int kThreads = kWaves * kWave;
@@ -31,34 +50,72 @@ struct AttnShape {
   static constexpr int kDT = D / 32;    // 32-wide head_dim tiles
   static constexpr int kKSD = D / 16;   // MFMA k-steps over head_dim
   static constexpr int kKSB = B / 16;   // MFMA k-steps over keys
-  static constexpr int kKStride = D + 8;  // LDS row pitch of K (bf16), 16 B pad
-  static constexpr int kVStride = B + 8;  // LDS row pitch of V^T (bf16)
-  static constexpr int kKChunks = B * D / 8 / kThreads;        // 16-byte K loads per thread
-  static constexpr int kVGroups = (B / 4) * (D / 8) / kThreads;  // 4-key x 8-d V groups per thread
+  static constexpr int kTile = B * D;   // elements of a K or V^T tile
+  static constexpr int kCprK = D / 8;   // 16-byte chunks per K row
+  static constexpr int kCprV = B / 8;   // 16-byte chunks per V^T row
+  static constexpr int kLoads = kTile * 2 / 16 / kThreads;  // 16-byte loads per lane per tile
 };
 
-__device__ __forceinline__ int vt_pos(int key) {
-  // position of `key` inside its 16-key group of V^T: swap groups 1 and 2
-  const int g4 = (key >> 2) & 3;
-  const int sw = ((g4 & 1) << 1) | (g4 >> 1);
-  return (key & ~15) | (sw << 2) | (key & 3);
+// V [H, N, D] -> V^T [H, D, NB*B] with vt_pos order inside every 16 keys and
+// zeros past the last token: the operand layout of O^T = V^T P^T.
+template <int D, int B>
+__global__ __launch_bounds__(256) void vt_kernel(const uint16_t* __restrict__ v,
+                                                 uint16_t* __restrict__ vt, int N, int NB) {
+  __shared__ uint16_t tile[B][D + 2];
+  const int J = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int kbase = J * B, bJ = min(B, N - kbase);
+  const size_t np = static_cast<size_t>(NB) * B;
+  for (int c = tid; c < B * D / 8; c += 256) {
+    const int r = c / (D / 8), c8 = c % (D / 8);
+    u32x4 x = r < bJ ? *reinterpret_cast<const u32x4*>(v + (static_cast<size_t>(h) * N + kbase + r) * D + c8 * 8)
+                     : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      tile[r][c8 * 8 + 2 * e] = static_cast<uint16_t>(x[e] & 0xffffu);
+      tile[r][c8 * 8 + 2 * e + 1] = static_cast<uint16_t>(x[e] >> 16);
+    }
+  }
+  __syncthreads();
+  for (int c = tid; c < D * B / 8; c += 256) {
+    const int d = c / (B / 8), p8 = c % (B / 8);
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo = tile[vt_pos(8 * p8 + 2 * e)][d];
+      const uint32_t hi = tile[vt_pos(8 * p8 + 2 * e + 1)][d];
+      o[e] = lo | (hi << 16);
+    }
+    *reinterpret_cast<u32x4*>(vt + (static_cast<size_t>(h) * D + d) * np + kbase + 8 * p8) = o;
+  }
 }
 
-template <int D, int B>
-__global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
+// One workgroup per (head, query block): B/32 waves, 32 query rows each.
+// K and V^T tiles stream global -> LDS directly (16-byte loads whose LDS
+// destinations are consecutive per wave; each lane picks the global chunk
+// that belongs at its slot of the swizzled layout).  NBUF = 2: the next
+// tile loads while the current one is used (one workgroup per CU);
+// NBUF = 1: single buffer, two workgroups per CU cover each other.
+template <int D, int B, int NBUF>
+__global__ __launch_bounds__(2 * B, 3 - NBUF) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ v, const int* __restrict__ counts,
+    const uint16_t* __restrict__ vt, const int* __restrict__ counts,
     const int* __restrict__ block_idx, uint16_t* __restrict__ out,
-    float* __restrict__ lse, int N, int NB, float scale_log2) {
-  using S = AttnShape<D, B>;
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[B * S::kKStride];
-  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * S::kVStride];
+    float* __restrict__ lse, int H, int N, int NB, float scale_log2) {
+  using S = AttnShape<D, B, NBUF>;
+  __shared__ __attribute__((aligned(1024))) uint16_t smem[NBUF][2][S::kTile];
 
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = tile / NB, I = tile - h * NB;
+  // Head-synchronous schedule: workgroup ids go round-robin over the 8 XCDs;
+  // XCD x takes the x-th contiguous eighth of the query blocks of one head
+  // after another, so all XCDs share one head's K/V at a time.
+  const int per_xcd = (NB + 7) / 8;
+  const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
+  const int h = slot / per_xcd, I = xcd * per_xcd + slot % per_xcd;
+  if (h >= H || I >= NB) return;
+
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hl = lane >> 5, col = lane & 31;
   const size_t head_off = static_cast<size_t>(h) * N * D;
+  const size_t np = static_cast<size_t>(NB) * B;
   const int qrow = I * B + wave * 32 + col;
 
   bf16x8 qf[S::kKSD];
@@ -72,78 +129,67 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
     }
   }
 
+  const int cnt = counts[h * NB + I];
+  const int* list = block_idx + (static_cast<size_t>(h) * NB + I) * NB;
+  const uint16_t* kh = k + head_off;
+  const uint16_t* vth = vt + static_cast<size_t>(h) * D * np;
+
+  auto issue = [&](int J, int buf) {
+    const int kbase = J * B, last = min(B, N - kbase) - 1;
+#pragma unroll
+    for (int i = 0; i < S::kLoads; ++i) {
+      const int blk = wave * S::kLoads + i;          // 1 KB block of the tile
+      const int pc = blk * 64 + lane;                // physical chunk
+      {
+        const int r = pc / S::kCprK, c = (pc % S::kCprK) ^ swz<S::kCprK>(r);
+        const uint16_t* src = kh + static_cast<size_t>(kbase + min(r, last)) * D + c * 8;
+        __builtin_amdgcn_global_load_lds((const gvoid*)src, (lvoid*)(&smem[buf][0][blk * 512]), 16, 0, 0);
+      }
+      {
+        const int r = pc / S::kCprV, c = (pc % S::kCprV) ^ swz<S::kCprV>(r);
+        const uint16_t* src = vth + static_cast<size_t>(r) * np + kbase + c * 8;
+        __builtin_amdgcn_global_load_lds((const gvoid*)src, (lvoid*)(&smem[buf][1][blk * 512]), 16, 0, 0);
+      }
+    }
+  };
+
   f32x16 oacc[S::kDT];
 #pragma unroll
   for (int t = 0; t < S::kDT; ++t) oacc[t] = f32x16{};
   float m_run = -INFINITY;  // reference maximum, log2 units
-  float l_run = 0.f;        // this lane's share of the row sum
+  float l_part[4] = {0.f, 0.f, 0.f, 0.f};
 
-  const int cnt = counts[h * NB + I];
-  const int* list = block_idx + (static_cast<size_t>(h) * NB + I) * NB;
-  const uint16_t* kh = k + head_off;
-  const uint16_t* vh = v + head_off;
-
-  for (int it = 0; it < cnt; ++it) {
-    const int J = list[it];
-    const int kbase = J * B;
-    const int bJ = min(B, N - kbase);
-
-    u32x4 kr[S::kKChunks];
-#pragma unroll
-    for (int i = 0; i < S::kKChunks; ++i) {
-      const int c = tid + i * S::kThreads;
-      const int row = c / (D / 8), c8 = c % (D / 8);
-      kr[i] = row < bJ ? *reinterpret_cast<const u32x4*>(kh + static_cast<size_t>(kbase + row) * D + c8 * 8)
-                       : u32x4{0, 0, 0, 0};
-    }
-    u32x4 vr[S::kVGroups][4];
-#pragma unroll
-    for (int i = 0; i < S::kVGroups; ++i) {
-      const int gi = tid + i * S::kThreads;
-      const int c8 = gi % (D / 8), g = gi / (D / 8);
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        const int row = 4 * g + r;
-        vr[i][r] = row < bJ ? *reinterpret_cast<const u32x4*>(vh + static_cast<size_t>(kbase + row) * D + c8 * 8)
-                            : u32x4{0, 0, 0, 0};
-      }
-    }
-    __syncthreads();  // previous block's LDS reads are done
-#pragma unroll
-    for (int i = 0; i < S::kKChunks; ++i) {
-      const int c = tid + i * S::kThreads;
-      const int row = c / (D / 8), c8 = c % (D / 8);
-      *reinterpret_cast<u32x4*>(&Ks[row * S::kKStride + c8 * 8]) = kr[i];
-    }
-#pragma unroll
-    for (int i = 0; i < S::kVGroups; ++i) {
-      const int gi = tid + i * S::kThreads;
-      const int c8 = gi % (D / 8), g = gi / (D / 8);
-      const int pos = vt_pos(4 * g);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t a0 = vr[i][0][e], a1 = vr[i][1][e], a2 = vr[i][2][e], a3 = vr[i][3][e];
-        u32x2 lo, hi;
-        lo[0] = (a0 & 0xffffu) | (a1 << 16);
-        lo[1] = (a2 & 0xffffu) | (a3 << 16);
-        hi[0] = (a0 >> 16) | (a1 & 0xffff0000u);
-        hi[1] = (a2 >> 16) | (a3 & 0xffff0000u);
-        const int d = c8 * 8 + 2 * e;
-        *reinterpret_cast<u32x2*>(&Vt[d * S::kVStride + pos]) = lo;
-        *reinterpret_cast<u32x2*>(&Vt[(d + 1) * S::kVStride + pos]) = hi;
-      }
-    }
+  if (NBUF == 2 && cnt > 0) {
+    issue(list[0], 0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
+  }
+  for (int it = 0; it < cnt; ++it) {
+    const int cur = NBUF == 2 ? (it & 1) : 0;
+    const int J = list[it];
+    const int bJ = min(B, N - J * B);
+    if (NBUF == 2) {
+      if (it + 1 < cnt) issue(list[it + 1], cur ^ 1);
+    } else {
+      __syncthreads();  // every wave is done with the buffer
+      issue(J, 0);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+    }
+    const char* kt = reinterpret_cast<const char*>(smem[cur][0]);
+    const char* vs = reinterpret_cast<const char*>(smem[cur][1]);
 
     f32x16 sacc[S::kKT];
 #pragma unroll
     for (int t = 0; t < S::kKT; ++t) {
+      const int r = 32 * t + col;
+      bf16x8 a[S::kKSD];
+#pragma unroll
+      for (int s = 0; s < S::kKSD; ++s)
+        a[s] = *reinterpret_cast<const bf16x8*>(kt + r * (2 * D) + (((2 * s + hl) ^ swz<S::kCprK>(r)) * 16));
       sacc[t] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < S::kKSD; ++s) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Ks[(32 * t + col) * S::kKStride + 16 * s + 8 * hl]);
-        sacc[t] = mfma32(a, qf[s], sacc[t]);
-      }
+      for (int s = 0; s < S::kKSD; ++s) sacc[t] = mfma32(a[s], qf[s], sacc[t]);
     }
     if (bJ < B) {
 #pragma unroll
@@ -163,7 +209,8 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
     if (__any(need)) {
       const float m_new = need ? m_blk : m_run;
       const float alpha = exp2f(m_run - m_new);
-      l_run *= alpha;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) l_part[e] *= alpha;
 #pragma unroll
       for (int t = 0; t < S::kDT; ++t) oacc[t] *= alpha;
       m_run = m_new;
@@ -174,20 +221,27 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][r], scale_log2, -m_run));
-        l_run += p;
+        l_part[r & 3] += p;
         pb[2 * t + (r >> 3)][r & 7] = static_cast<__bf16>(p);
       }
     }
 #pragma unroll
     for (int dt = 0; dt < S::kDT; ++dt) {
+      const int r = 32 * dt + col;
+      bf16x8 a[S::kKSB];
 #pragma unroll
-      for (int u = 0; u < S::kKSB; ++u) {
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&Vt[(32 * dt + col) * S::kVStride + 16 * u + 8 * hl]);
-        oacc[dt] = mfma32(a, pb[u], oacc[dt]);
-      }
+      for (int u = 0; u < S::kKSB; ++u)
+        a[u] = *reinterpret_cast<const bf16x8*>(vs + r * (2 * B) + (((2 * u + hl) ^ swz<S::kCprV>(r)) * 16));
+#pragma unroll
+      for (int u = 0; u < S::kKSB; ++u) oacc[dt] = mfma32(a[u], pb[u], oacc[dt]);
+    }
+    if (NBUF == 2) {
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();  // next tile landed; every wave is done with this one
     }
   }
 
+  const float l_run = (l_part[0] + l_part[1]) + (l_part[2] + l_part[3]);
   const float l_tot = l_run + __shfl_xor(l_run, 32);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < N) {
@@ -282,18 +336,23 @@ __global__ __launch_bounds__(B) void attn_f32_kernel(
 
 template <int D, int B>
 hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const void* v,
-                         const int* counts, const int* idx, void* out, float* lse,
+                         const int* counts, const int* idx, void* out, float* lse, void* ws,
                          hipStream_t stream) {
-  const int grid = p.heads * p.nb;
   const float sl2 = p.scale * kLog2e;
   if (p.dtype == 0) {
-    using S = AttnShape<D, B>;
-    hipLaunchKernelGGL((attn_bf16_kernel<D, B>), dim3(grid), dim3(S::kThreads), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                       static_cast<const uint16_t*>(v), counts, idx, static_cast<uint16_t*>(out),
-                       lse, p.tokens, p.nb, sl2);
+    constexpr int kNbuf = 2;
+    using S = AttnShape<D, B, kNbuf>;
+    uint16_t* vt = static_cast<uint16_t*>(ws);
+    hipLaunchKernelGGL((vt_kernel<D, B>), dim3(p.nb, p.heads), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(v), vt, p.tokens, p.nb);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int grid = 8 * ((p.nb + 7) / 8) * p.heads;
+    hipLaunchKernelGGL((attn_bf16_kernel<D, B, kNbuf>), dim3(grid), dim3(S::kThreads), 0, stream,
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt, counts,
+                       idx, static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2);
   } else {
-    hipLaunchKernelGGL((attn_f32_kernel<D, B>), dim3(grid), dim3(B), 0, stream,
+    hipLaunchKernelGGL((attn_f32_kernel<D, B>), dim3(p.heads * p.nb), dim3(B), 0, stream,
                        static_cast<const float*>(q), static_cast<const float*>(k),
                        static_cast<const float*>(v), counts, idx, static_cast<float*>(out),
                        lse, p.tokens, p.nb, sl2);
@@ -303,13 +362,18 @@ hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const v
 
 }  // namespace
 
+size_t attn_ws_bytes(const Problem& p) {
+  if (p.dtype != 0) return 0;
+  return (sizeof(uint16_t) * p.heads * p.head_dim * static_cast<size_t>(p.nb) * p.block + 255) / 256 * 256;
+}
+
 hipError_t launch_attention(const Problem& p, const void* q, const void* k, const void* v,
-                            const int* counts, const int* idx, void* out, float* lse,
+                            const int* counts, const int* idx, void* out, float* lse, void* ws,
                             hipStream_t stream) {
-  if (p.head_dim == 128 && p.block == 128) return launch_attn_t<128, 128>(p, q, k, v, counts, idx, out, lse, stream);
-  if (p.head_dim == 128 && p.block == 64) return launch_attn_t<128, 64>(p, q, k, v, counts, idx, out, lse, stream);
-  if (p.head_dim == 64 && p.block == 128) return launch_attn_t<64, 128>(p, q, k, v, counts, idx, out, lse, stream);
-  return launch_attn_t<64, 64>(p, q, k, v, counts, idx, out, lse, stream);
+  if (p.head_dim == 128 && p.block == 128) return launch_attn_t<128, 128>(p, q, k, v, counts, idx, out, lse, ws, stream);
+  if (p.head_dim == 128 && p.block == 64) return launch_attn_t<128, 64>(p, q, k, v, counts, idx, out, lse, ws, stream);
+  if (p.head_dim == 64 && p.block == 128) return launch_attn_t<64, 128>(p, q, k, v, counts, idx, out, lse, ws, stream);
+  return launch_attn_t<64, 64>(p, q, k, v, counts, idx, out, lse, ws, stream);
 }
 
 }  // namespace rsa

@@ -39,8 +39,10 @@ hipError_t launch_select(const Problem& p, const float* scores, const float* top
 hipError_t launch_drift(const Problem& p, const void* q, const void* k, void* q_ref,
                         void* k_ref, float threshold, int update_ref, float* drift,
                         uint8_t* refresh, void* ws, hipStream_t stream);
+// bf16 attention workspace: V transposed to [H, D, NB*B] (0 for fp32).
+size_t attn_ws_bytes(const Problem& p);
 hipError_t launch_attention(const Problem& p, const void* q, const void* k, const void* v,
-                            const int* counts, const int* idx, void* out, float* lse,
+                            const int* counts, const int* idx, void* out, float* lse, void* ws,
                             hipStream_t stream);
 
 }  // namespace rsa

@@ -199,7 +199,9 @@ rsa_status rsa_mask_drift(const rsa_problem* p, const void* q, const void* k,
  * lse: [heads, tokens] fp32 output or NULL.
  * bf16 inputs: bf16 matrix-core products with fp32 accumulation and an fp32
  *   online softmax; fp32 inputs: fp32 arithmetic throughout.
- * ws / ws_bytes: unused (rsa_workspace_bytes returns 0); may be NULL / 0.
+ * ws / ws_bytes: at least rsa_workspace_bytes(p, RSA_OP_ATTN) bytes, 256-byte
+ *   aligned (bf16: heads * head_dim * NB * block * 2 bytes, where v is
+ *   re-laid out key-major for the matrix cores; fp32: 0, may be NULL / 0).
  * Out-of-range counts or indices are not checked on the device: the caller
  * guarantees them (rsa_select_topp's outputs always satisfy them).
  */

@@ -61,7 +61,9 @@ def test_workspace_sizes():
     want = al(4 * 40 * 591 * 128) + al(4 * 40 * 591) + 2 * al(2 * 40 * nbp * 128) + al(4 * 40)
     assert B.workspace_bytes(p, B.OP_SCORE) == want
     assert B.workspace_bytes(p, B.OP_DRIFT) == 8 * 2 * 64 * 40
-    assert B.workspace_bytes(p, B.OP_SELECT) == 0 and B.workspace_bytes(p, B.OP_ATTN) == 0
+    assert B.workspace_bytes(p, B.OP_SELECT) == 0
+    assert B.workspace_bytes(p, B.OP_ATTN) == 2 * 40 * 128 * 591 * 128        # v re-laid out key-major
+    assert B.workspace_bytes(prob(heads=40, grid=(21, 45, 80), b=128, dtype=1), B.OP_ATTN) == 0
     assert B.workspace_bytes(prob(d=96), B.OP_SCORE) == 0          # invalid problem -> 0
 
 
@@ -109,7 +111,7 @@ def test_alignment(lib):
     b = Buf()
     mis = ctypes.c_void_p(b.view.ctypes.data + 8)
     assert lib.rsa_block_sparse_attn(ctypes.byref(p), mis, b.ptr, b.ptr, b.ptr, b.ptr, b.ptr, None,
-                                     None, 0, None) == ALIGN
+                                     b.ptr, 1 << 30, None) == ALIGN
     assert lib.rsa_score_blocks(ctypes.byref(p), b.ptr, b.ptr, None, mis, b.ptr, 1 << 30, None) == ALIGN
     assert b.untouched()
 
@@ -122,6 +124,9 @@ def test_workspace_checks(lib):
     assert lib.rsa_score_blocks(ctypes.byref(p), b.ptr, b.ptr, None, b.ptr, b.ptr, need - 1, None) == WS
     mis = ctypes.c_void_p(b.view.ctypes.data + 16)
     assert lib.rsa_score_blocks(ctypes.byref(p), b.ptr, b.ptr, None, b.ptr, mis, need, None) == WS
+    aneed = B.workspace_bytes(p, B.OP_ATTN)
+    assert lib.rsa_block_sparse_attn(ctypes.byref(p), b.ptr, b.ptr, b.ptr, b.ptr, b.ptr, b.ptr, None,
+                                     b.ptr, aneed - 1, None) == WS
     dneed = B.workspace_bytes(p, B.OP_DRIFT)
     assert lib.rsa_mask_drift(ctypes.byref(p), b.ptr, b.ptr, b.ptr, b.ptr, 0.05, 1, b.ptr, b.ptr,
                               b.ptr, dneed - 8, None) == WS
