@@ -2,7 +2,7 @@
 // the caller's stream.  Declarations and contracts are in include/rsa.h.
 #include <cmath>
 
-#include "../../include/rsa.h"
+#include "rsa.h"
 #include "kernels.h"
 
 namespace {

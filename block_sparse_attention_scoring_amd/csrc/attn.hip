@@ -42,18 +42,22 @@ __device__ __forceinline__ int swz(int r) {
   return CPR == 16 ? (r & 15) : ((r >> 1) & 7);
 }
 
-template <int D, int B, int NBUF>
+// Work of one workgroup: B/32 waves (32 query rows each) against key
+// sub-tiles of KS keys; NBUF LDS buffers per operand.
+template <int D, int B, int KS, int NBUF>
 struct AttnShape {
   static constexpr int kWaves = B / 32;
   static constexpr int kThreads = kWaves * kWave;
-  static constexpr int kKT = B / 32;    // 32-key tiles of a key block
+  static constexpr int kKT = KS / 32;   // 32-key tiles of a sub-tile
   static constexpr int kDT = D / 32;    // 32-wide head_dim tiles
   static constexpr int kKSD = D / 16;   // MFMA k-steps over head_dim
-  static constexpr int kKSB = B / 16;   // MFMA k-steps over keys
-  static constexpr int kTile = B * D;   // elements of a K or V^T tile
+  static constexpr int kKSK = KS / 16;  // MFMA k-steps over the sub-tile's keys
+  static constexpr int kTile = KS * D;  // elements of a K or V^T sub-tile
   static constexpr int kCprK = D / 8;   // 16-byte chunks per K row
-  static constexpr int kCprV = B / 8;   // 16-byte chunks per V^T row
-  static constexpr int kLoads = kTile * 2 / 16 / kThreads;  // 16-byte loads per lane per tile
+  static constexpr int kCprV = KS / 8;  // 16-byte chunks per V^T row
+  static constexpr int kLoads = kTile * 2 / 16 / kThreads;  // 16-byte loads per lane per operand
+  static constexpr int kSub = B / KS;   // sub-tiles per key block
+  static_assert(kLoads >= 1 && kTile * 2 % (16 * kThreads) == 0, "tile not divisible");
 };
 
 // V [H, N, D] -> V^T [H, D, NB*B] with vt_pos order inside every 16 keys and
@@ -89,20 +93,22 @@ __global__ __launch_bounds__(256) void vt_kernel(const uint16_t* __restrict__ v,
   }
 }
 
-// One workgroup per (head, query block): B/32 waves, 32 query rows each.
-// K and V^T tiles stream global -> LDS directly (16-byte loads whose LDS
-// destinations are consecutive per wave; each lane picks the global chunk
-// that belongs at its slot of the swizzled layout).  NBUF = 2: the next
-// tile loads while the current one is used (one workgroup per CU);
-// NBUF = 1: single buffer, two workgroups per CU cover each other.
-template <int D, int B, int NBUF>
-__global__ __launch_bounds__(2 * B, 3 - NBUF) void attn_bf16_kernel(
+// One workgroup per (head, query block): B/32 waves, 32 query rows each,
+// walking its key blocks in sub-tiles of KS keys.  K and V^T sub-tiles
+// stream global -> LDS directly (16-byte loads whose LDS destinations are
+// consecutive per wave; each lane picks the global chunk that belongs at its
+// slot of the swizzled layout).  NBUF = 2: the next sub-tile loads while the
+// current one is used.  Two or more workgroups share a CU, so one's softmax
+// (VALU) overlaps another's matrix products on every SIMD.
+template <int D, int B, int KS, int NBUF>
+__global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const int* __restrict__ counts,
     const int* __restrict__ block_idx, uint16_t* __restrict__ out,
     float* __restrict__ lse, int H, int N, int NB, float scale_log2) {
-  using S = AttnShape<D, B, NBUF>;
-  __shared__ __attribute__((aligned(1024))) uint16_t smem[NBUF][2][S::kTile];
+  using S = AttnShape<D, B, KS, NBUF>;
+  __shared__ __attribute__((aligned(1024))) uint16_t kbuf[NBUF][S::kTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t vbuf[NBUF][S::kTile];
 
   // Head-synchronous schedule: workgroup ids go round-robin over the 8 XCDs;
   // XCD x takes the x-th contiguous eighth of the query blocks of one head
@@ -130,25 +136,30 @@ __global__ __launch_bounds__(2 * B, 3 - NBUF) void attn_bf16_kernel(
   }
 
   const int cnt = counts[h * NB + I];
+  const int total = cnt * S::kSub;  // sub-tiles to visit
   const int* list = block_idx + (static_cast<size_t>(h) * NB + I) * NB;
   const uint16_t* kh = k + head_off;
   const uint16_t* vth = vt + static_cast<size_t>(h) * D * np;
 
-  auto issue = [&](int J, int buf) {
-    const int kbase = J * B, last = min(B, N - kbase) - 1;
+  // first key and number of real keys of sub-tile u
+  auto sub_base = [&](int u) { return list[u / S::kSub] * B + (u % S::kSub) * KS; };
+
+  auto issue = [&](int u, int buf) {
+    const int kbase = sub_base(u);
+    const int last = max(0, min(KS, N - kbase) - 1);
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
-      const int blk = wave * S::kLoads + i;          // 1 KB block of the tile
-      const int pc = blk * 64 + lane;                // physical chunk
+      const int blk = wave * S::kLoads + i;  // 1 KB block of the sub-tile
+      const int pc = blk * 64 + lane;        // physical 16-byte chunk
       {
         const int r = pc / S::kCprK, c = (pc % S::kCprK) ^ swz<S::kCprK>(r);
-        const uint16_t* src = kh + static_cast<size_t>(kbase + min(r, last)) * D + c * 8;
-        __builtin_amdgcn_global_load_lds((const gvoid*)src, (lvoid*)(&smem[buf][0][blk * 512]), 16, 0, 0);
+        const uint16_t* src = kh + static_cast<size_t>(min(kbase + min(r, last), N - 1)) * D + c * 8;
+        __builtin_amdgcn_global_load_lds((const gvoid*)src, (lvoid*)(&kbuf[buf][blk * 512]), 16, 0, 0);
       }
       {
         const int r = pc / S::kCprV, c = (pc % S::kCprV) ^ swz<S::kCprV>(r);
         const uint16_t* src = vth + static_cast<size_t>(r) * np + kbase + c * 8;
-        __builtin_amdgcn_global_load_lds((const gvoid*)src, (lvoid*)(&smem[buf][1][blk * 512]), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const gvoid*)src, (lvoid*)(&vbuf[buf][blk * 512]), 16, 0, 0);
       }
     }
   };
@@ -159,25 +170,24 @@ __global__ __launch_bounds__(2 * B, 3 - NBUF) void attn_bf16_kernel(
   float m_run = -INFINITY;  // reference maximum, log2 units
   float l_part[4] = {0.f, 0.f, 0.f, 0.f};
 
-  if (NBUF == 2 && cnt > 0) {
-    issue(list[0], 0);
+  if (NBUF == 2 && total > 0) {
+    issue(0, 0);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
-  for (int it = 0; it < cnt; ++it) {
-    const int cur = NBUF == 2 ? (it & 1) : 0;
-    const int J = list[it];
-    const int bJ = min(B, N - J * B);
+  for (int u = 0; u < total; ++u) {
+    const int cur = NBUF == 2 ? (u & 1) : 0;
     if (NBUF == 2) {
-      if (it + 1 < cnt) issue(list[it + 1], cur ^ 1);
+      if (u + 1 < total) issue(u + 1, cur ^ 1);
     } else {
-      __syncthreads();  // every wave is done with the buffer
-      issue(J, 0);
+      __syncthreads();  // every wave is done with the buffers
+      issue(u, 0);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
       __syncthreads();
     }
-    const char* kt = reinterpret_cast<const char*>(smem[cur][0]);
-    const char* vs = reinterpret_cast<const char*>(smem[cur][1]);
+    const int valid = N - sub_base(u);  // real keys of this sub-tile (>= KS on all but the tail)
+    const char* kt = reinterpret_cast<const char*>(kbuf[cur]);
+    const char* vs = reinterpret_cast<const char*>(vbuf[cur]);
 
     f32x16 sacc[S::kKT];
 #pragma unroll
@@ -191,12 +201,12 @@ __global__ __launch_bounds__(2 * B, 3 - NBUF) void attn_bf16_kernel(
 #pragma unroll
       for (int s = 0; s < S::kKSD; ++s) sacc[t] = mfma32(a[s], qf[s], sacc[t]);
     }
-    if (bJ < B) {
+    if (valid < KS) {
 #pragma unroll
       for (int t = 0; t < S::kKT; ++t)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (32 * t + acc_row(r, hl) >= bJ) sacc[t][r] = -INFINITY;
+          if (32 * t + acc_row(r, hl) >= valid) sacc[t][r] = -INFINITY;
     }
     float mx = -INFINITY;
 #pragma unroll
@@ -206,21 +216,21 @@ __global__ __launch_bounds__(2 * B, 3 - NBUF) void attn_bf16_kernel(
     mx = fmaxf(mx, __shfl_xor(mx, 32));
     const float m_blk = mx * scale_log2;
     const bool need = m_blk > m_run + 8.f;
-    if (__any(need)) {
-      const float m_new = need ? m_blk : m_run;
-      const float alpha = exp2f(m_run - m_new);
+    const float m_use = need ? m_blk : m_run;
+    const float alpha = need ? exp2f(m_run - m_use) : 1.f;
+    m_run = m_use;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) l_part[e] *= alpha;
+    for (int e = 0; e < 4; ++e) l_part[e] *= alpha;
+    if (__any(need)) {
 #pragma unroll
       for (int t = 0; t < S::kDT; ++t) oacc[t] *= alpha;
-      m_run = m_new;
     }
-    bf16x8 pb[S::kKSB];
+    bf16x8 pb[S::kKSK];
 #pragma unroll
     for (int t = 0; t < S::kKT; ++t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][r], scale_log2, -m_run));
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][r], scale_log2, -m_use));
         l_part[r & 3] += p;
         pb[2 * t + (r >> 3)][r & 7] = static_cast<__bf16>(p);
       }
@@ -228,16 +238,16 @@ __global__ __launch_bounds__(2 * B, 3 - NBUF) void attn_bf16_kernel(
 #pragma unroll
     for (int dt = 0; dt < S::kDT; ++dt) {
       const int r = 32 * dt + col;
-      bf16x8 a[S::kKSB];
+      bf16x8 a[S::kKSK];
 #pragma unroll
-      for (int u = 0; u < S::kKSB; ++u)
-        a[u] = *reinterpret_cast<const bf16x8*>(vs + r * (2 * B) + (((2 * u + hl) ^ swz<S::kCprV>(r)) * 16));
+      for (int w = 0; w < S::kKSK; ++w)
+        a[w] = *reinterpret_cast<const bf16x8*>(vs + r * (2 * KS) + (((2 * w + hl) ^ swz<S::kCprV>(r)) * 16));
 #pragma unroll
-      for (int u = 0; u < S::kKSB; ++u) oacc[dt] = mfma32(a[u], pb[u], oacc[dt]);
+      for (int w = 0; w < S::kKSK; ++w) oacc[dt] = mfma32(a[w], pb[w], oacc[dt]);
     }
     if (NBUF == 2) {
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();  // next tile landed; every wave is done with this one
+      __syncthreads();  // next sub-tile landed; every wave is done with this one
     }
   }
 
@@ -340,15 +350,16 @@ hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const v
                          hipStream_t stream) {
   const float sl2 = p.scale * kLog2e;
   if (p.dtype == 0) {
-    constexpr int kNbuf = 2;
-    using S = AttnShape<D, B, kNbuf>;
+    // 64-key sub-tiles; double buffers when 128 query rows fill a workgroup
+    constexpr int kKs = 64, kNbuf = B == 128 ? 2 : 1;
+    using S = AttnShape<D, B, kKs, kNbuf>;
     uint16_t* vt = static_cast<uint16_t*>(ws);
     hipLaunchKernelGGL((vt_kernel<D, B>), dim3(p.nb, p.heads), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(v), vt, p.tokens, p.nb);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int grid = 8 * ((p.nb + 7) / 8) * p.heads;
-    hipLaunchKernelGGL((attn_bf16_kernel<D, B, kNbuf>), dim3(grid), dim3(S::kThreads), 0, stream,
+    hipLaunchKernelGGL((attn_bf16_kernel<D, B, kKs, kNbuf>), dim3(grid), dim3(S::kThreads), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt, counts,
                        idx, static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2);
   } else {
