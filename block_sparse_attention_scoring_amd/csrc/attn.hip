@@ -39,6 +39,7 @@ __host__ __device__ __forceinline__ int vt_pos(int key) {
 // 16 consecutive rows read at one logical chunk hit 16 distinct bank groups.
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
+  static_assert(CPR == 8 || CPR == 16, "swizzle defined for rows of 8 or 16 chunks");
   return CPR == 16 ? (r & 15) : ((r >> 1) & 7);
 }
 

@@ -140,6 +140,40 @@ __global__ __launch_bounds__(256) void split_kernel(
 }
 
 // ---------------------------------------------------------------- score
+// Exchange with the lane whose index (within its 32-lane half) differs in the
+// bits of `mask` (ds_swizzle bit mode: and 0x1f, or 0, xor mask).
+template <int mask>
+__device__ __forceinline__ float swap_lanes(float v) {
+  return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), (mask << 10) | 0x1f));
+}
+
+// Reduce-scatter of 16 values over 32 lanes (16 exchanges instead of 80):
+// returns, to lane `col`, the sum over the 32 lanes of v[col >> 1].
+__device__ __forceinline__ float reduce_scatter_32(const float (&v)[16], int col) {
+  float a[8];
+  const bool b4 = col & 16, b3 = col & 8, b2 = col & 4, b1 = col & 2;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const float keep = b4 ? v[j + 8] : v[j], send = b4 ? v[j] : v[j + 8];
+    a[j] = keep + swap_lanes<16>(send);
+  }
+  float b[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float keep = b3 ? a[j + 4] : a[j], send = b3 ? a[j] : a[j + 4];
+    b[j] = keep + swap_lanes<8>(send);
+  }
+  float c[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const float keep = b2 ? b[j + 2] : b[j], send = b2 ? b[j] : b[j + 2];
+    c[j] = keep + swap_lanes<4>(send);
+  }
+  const float keep = b1 ? c[1] : c[0], send = b1 ? c[0] : c[1];
+  const float d = keep + swap_lanes<2>(send);
+  return d + swap_lanes<1>(d);
+}
+
 template <typename T, int D, int B>
 struct ScoreShape {
   static constexpr bool kSplitQ = sizeof(T) == 4;  // fp32 queries: two fp16 terms
@@ -207,20 +241,21 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(
   const _Float16* kh_head = khi + static_cast<size_t>(h) * NBp * D;
   const _Float16* kl_head = klo + static_cast<size_t>(h) * NBp * D;
 
-  // logits of chunk c (32 key blocks) for query sub-tile st, raw units
+  // logits of chunk c (32 key blocks) for query sub-tile st, raw units; the
+  // hi and lo terms run as two independent accumulation chains
   auto logits = [&](const f16x8 (&ahi)[S::kKS], const f16x8 (&alo)[S::kKS], int st) {
-    f32x16 acc = f32x16{};
+    f32x16 acc_hi = f32x16{}, acc_lo = f32x16{};
 #pragma unroll
     for (int s = 0; s < S::kKS; ++s) {
       const f16x8 b = *reinterpret_cast<const f16x8*>(&Qh[(32 * st + col) * S::kQStride + 16 * s + 8 * hl]);
-      acc = mfma32(ahi[s], b, acc);
-      acc = mfma32(alo[s], b, acc);
+      acc_hi = mfma32(ahi[s], b, acc_hi);
+      acc_lo = mfma32(alo[s], b, acc_lo);
       if constexpr (S::kSplitQ) {
         const f16x8 bl = *reinterpret_cast<const f16x8*>(&Ql[(32 * st + col) * S::kQStride + 16 * s + 8 * hl]);
-        acc = mfma32(ahi[s], bl, acc);
+        acc_lo = mfma32(ahi[s], bl, acc_lo);
       }
     }
-    return acc;
+    return acc_hi + acc_lo;
   };
   auto load_a = [&](int c, f16x8 (&ahi)[S::kKS], f16x8 (&alo)[S::kKS]) {
     const size_t row = static_cast<size_t>(32 * c + col) * D + 8 * hl;
@@ -244,6 +279,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(
     const bool tail = 32 * c + 32 > NB;
 #pragma unroll
     for (int st = 0; st < S::kSub; ++st) {
+      __builtin_amdgcn_sched_barrier(0);  // one sub-tile's registers live at a time
       f32x16 acc = logits(ahi, alo, st);
       if (tail) {
 #pragma unroll
@@ -303,6 +339,7 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(
     for (int r = 0; r < 16; ++r) colsum[r] = 0.f;
 #pragma unroll
     for (int st = 0; st < S::kSub; ++st) {
+      __builtin_amdgcn_sched_barrier(0);  // one sub-tile's registers live at a time
       f32x16 acc = logits(ahi, alo, st);
       if (tail) {
 #pragma unroll
@@ -312,19 +349,14 @@ __global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) colsum[r] += __builtin_amdgcn_exp2f(fmaf(acc[r], sc[st], rm[st])) * rw[st];
     }
-    // sum over the 32 query rows held by the lanes of this half
-#pragma unroll
-    for (int o = 1; o < 32; o <<= 1) {
-#pragma unroll
-      for (int r = 0; r < 16; ++r) colsum[r] += __shfl_xor(colsum[r], o);
-    }
-    if (col < 16) {
-      float val = 0.f;
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (col == r) val = colsum[r];
-      const int J = 32 * c + acc_row(col, hl);
-      if (J < NB) srow[J] = val;
+    // Sum over the 32 query rows held by the 32 lanes of this half, as a
+    // reduce-scatter: at the exchange over lane bit b a lane keeps the half of
+    // its values that matches its bit and adds the partner's copy of them.
+    // Lane `col` ends with the total of accumulator register col >> 1.
+    const float total = reduce_scatter_32(colsum, col);
+    if ((col & 1) == 0) {
+      const int J = 32 * c + acc_row(col >> 1, hl);
+      if (J < NB) srow[J] = total;
     }
   }
 }

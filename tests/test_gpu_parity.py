@@ -49,6 +49,7 @@ CASES = {
     "bf16_d128_b128": (2, (6, 20, 83), 128, 128, "bf16"),  # NB=78, last block 104
     "bf16_d64_b128": (2, (5, 16, 51), 64, 128, "bf16"),    # N=4080, NB=32, last block 112
     "bf16_d64_b64": (3, (4, 9, 37), 64, 64, "bf16"),       # N=1332, NB=21, last block 52
+    "bf16_d128_b128_short": (3, (2, 13, 31), 128, 128, "bf16"),  # N=806, NB=7, last block 38 (< 64)
     "fp32_tiny": (1, (4, 8, 8), 64, 64, "fp32"),           # the tiny workload itself
     "fp32_d128_b128": (2, (3, 10, 29), 128, 128, "fp32"),  # N=870, NB=7, last block 102
 }
