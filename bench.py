@@ -76,10 +76,14 @@ def executed_flops(counts, idx, wl):
     return float(4 * d * (key_tokens * bsz[None, :]).sum())
 
 
-def cpu_baseline(inp, wl, counts_gpu, idx_gpu, total_flops):
-    """Oracle on a bounded sample: head 0 scored + selected in full, attention on
-    24 evenly spaced query blocks of head 0 (the GPU's lists); extrapolated to
-    the whole step by head count (scoring) and executed FLOPs (attention)."""
+def cpu_baseline(inp, wl, counts_gpu, idx_gpu, total_flops, score_s=4.0, attn_s=10.0):
+    """The fp64 oracle on a time-bounded sample of the same step.
+
+    Scoring + top-p selection run on whole heads (0, 1, ...) until about
+    `score_s` seconds have passed; attention runs on seeded random query
+    blocks of all heads, with the GPU's block lists, until about `attn_s`
+    seconds.  The step time is extrapolated by head count (scoring) and by
+    executed FLOPs (attention)."""
     import numpy as np
     import oracle as O
     import workloads as W
@@ -88,32 +92,48 @@ def cpu_baseline(inp, wl, counts_gpu, idx_gpu, total_flops):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = os.cpu_count() or 1
-    q0, k0, v0 = W.to_f64(inp.q[0]), W.to_f64(inp.k[0]), W.to_f64(inp.v[0])
     scale = 1.0 / np.sqrt(wl.head_dim)
-    t0 = time.perf_counter()
-    s = O.score_head(q0, k0, wl.block, scale)
-    for i in range(wl.nblocks):
-        O.select_row(s[i], float(inp.top_p[0]))
-    t_ss = time.perf_counter() - t0
-    rows = np.linspace(0, wl.nblocks - 1, 24).astype(int)
-    lists = [idx_gpu[0, i, :counts_gpu[0, i]] for i in range(wl.nblocks)]
-    t0 = time.perf_counter()
-    O.block_sparse_attention(q0, k0, v0, wl.block, lists, scale, query_blocks=list(rows))
-    t_at = time.perf_counter() - t0
     nb, b, n = wl.nblocks, wl.block, wl.tokens
     bsz = np.full(nb, b, np.int64)
     bsz[-1] = n - b * (nb - 1)
-    sample_flops = float(sum(4 * wl.head_dim * bsz[i] * bsz[lists[i]].sum() for i in rows))
-    t_step = wl.heads * t_ss + t_at * total_flops / sample_flops
+
+    t_ss, heads_done = 0.0, 0
+    while heads_done < wl.heads and t_ss < score_s:
+        h = heads_done
+        q, k = W.to_f64(inp.q[h]), W.to_f64(inp.k[h])
+        t0 = time.perf_counter()
+        s = O.score_head(q, k, b, scale)
+        for i in range(nb):
+            O.select_row(s[i], float(inp.top_p[h]))
+        t_ss += time.perf_counter() - t0
+        heads_done += 1
+
+    rng = np.random.default_rng(7)
+    order = rng.permutation(wl.heads * nb)
+    t_at, sample_flops, blocks, cache = 0.0, 0.0, 0, {}
+    for t in order:
+        if t_at >= attn_s:
+            break
+        h, i = divmod(int(t), nb)
+        if h not in cache:
+            cache = {h: (W.to_f64(inp.q[h]), W.to_f64(inp.k[h]), W.to_f64(inp.v[h]))}
+        q, k, v = cache[h]
+        lst = idx_gpu[h, i, :counts_gpu[h, i]]
+        t0 = time.perf_counter()
+        O.block_sparse_attention(q, k, v, b, {i: lst}, scale, query_blocks=[i])
+        t_at += time.perf_counter() - t0
+        sample_flops += float(4 * wl.head_dim * bsz[i] * bsz[lst].sum())
+        blocks += 1
+    t_step = wl.heads * t_ss / heads_done + t_at * total_flops / sample_flops
     return {
         "value": round(total_flops / t_step / 1e12, 6),
         "unit": "TFLOP/s",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"fp64 oracle: head 0 of {wl.name} scored and top-p selected in full "
-                   f"({t_ss:.1f} s, x{wl.heads} heads) + attention on 24 of {nb} query blocks "
-                   f"of head 0 ({t_at:.1f} s, scaled by executed FLOPs); "
-                   f"extrapolated step {t_step:.0f} s"),
+        "sample": (f"fp64 oracle on {wl.name}: scoring + top-p selection of {heads_done} whole "
+                   f"head(s) ({t_ss:.1f} s, scaled x{wl.heads / heads_done:.1f} to all heads) and "
+                   f"attention of {blocks} random query blocks on the GPU's lists ({t_at:.1f} s, "
+                   f"scaled by executed FLOPs); extrapolated step {t_step:.0f} s"),
         "ms_per_step": round(t_step * 1e3, 1),
     }
 
@@ -168,6 +188,7 @@ def main():
     lse = torch.empty((wl.heads, wl.tokens), dtype=torch.float32, device=dev)
     ws_s = torch.empty(R.workspace_bytes(p, R.OP_SCORE), dtype=torch.uint8, device=dev)
     ws_d = torch.empty(R.workspace_bytes(p, R.OP_DRIFT), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(R.workspace_bytes(p, R.OP_ATTN), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream(dev)   # the library launches on this stream
 
     names = ("drift", "score", "select", "attn")
@@ -177,7 +198,7 @@ def main():
         lambda: R.score_blocks(q, k, p, out=scores, workspace=ws_s),
         lambda: R.select_topp(scores, top_p, p, mask=mask, counts=counts, block_idx=idx,
                               density=density),
-        lambda: R.block_sparse_attn(q, k, v, counts, idx, p, out=out, lse=lse),
+        lambda: R.block_sparse_attn(q, k, v, counts, idx, p, out=out, lse=lse, workspace=ws_a),
     )
 
     def step(events=None):
