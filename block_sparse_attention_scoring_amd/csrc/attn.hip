@@ -37,10 +37,15 @@ __host__ __device__ __forceinline__ int vt_pos(int key) {
 
 // XOR swizzle of the 16-byte chunks of an LDS tile row holding `cpr` chunks:
 // 16 consecutive rows read at one logical chunk hit 16 distinct bank groups.
+// Bank group of (row r, physical chunk p) is (r * CPR + p) mod 16; XOR-ing the
+// logical chunk with the row bits above the rows sharing 256 bytes makes the
+// 16 rows of one read distinct.
 template <int CPR>
 __device__ __forceinline__ int swz(int r) {
-  static_assert(CPR == 8 || CPR == 16, "swizzle defined for rows of 8 or 16 chunks");
-  return CPR == 16 ? (r & 15) : ((r >> 1) & 7);
+  static_assert(CPR == 4 || CPR == 8 || CPR == 16, "swizzle defined for rows of 4, 8 or 16 chunks");
+  if constexpr (CPR == 16) return r & 15;
+  else if constexpr (CPR == 8) return (r >> 1) & 7;
+  else return (r >> 2) & 3;
 }
 
 // Work of one workgroup: B/32 waves (32 query rows each) against key
@@ -108,8 +113,13 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
     const int* __restrict__ block_idx, uint16_t* __restrict__ out,
     float* __restrict__ lse, int H, int N, int NB, float scale_log2) {
   using S = AttnShape<D, B, KS, NBUF>;
-  __shared__ __attribute__((aligned(1024))) uint16_t kbuf[NBUF][S::kTile];
-  __shared__ __attribute__((aligned(1024))) uint16_t vbuf[NBUF][S::kTile];
+  static_assert(NBUF == 2, "two LDS slots");
+  // Slot arrays: K sub-tile at [0, kTile), V^T sub-tile after it.  Separate
+  // arrays, addressed with compile-time slot numbers, let the compiler see
+  // that the slot being filled is not the one being read, so it does not
+  // drain the prefetch before the matrix products.
+  __shared__ __attribute__((aligned(1024))) uint16_t slot0[2 * S::kTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t slot1[2 * S::kTile];
 
   // Head-synchronous schedule: workgroup ids go round-robin over the 8 XCDs;
   // XCD x takes the x-th contiguous eighth of the query blocks of one head
@@ -145,7 +155,7 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
   // first key and number of real keys of sub-tile u
   auto sub_base = [&](int u) { return list[u / S::kSub] * B + (u % S::kSub) * KS; };
 
-  auto issue = [&](int u, int buf) {
+  auto issue = [&](int u, uint16_t* dst) {
     const int kbase = sub_base(u);
     const int last = max(0, min(KS, N - kbase) - 1);
 #pragma unroll
@@ -155,12 +165,12 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
       {
         const int r = pc / S::kCprK, c = (pc % S::kCprK) ^ swz<S::kCprK>(r);
         const uint16_t* src = kh + static_cast<size_t>(min(kbase + min(r, last), N - 1)) * D + c * 8;
-        __builtin_amdgcn_global_load_lds((const gvoid*)src, (lvoid*)(&kbuf[buf][blk * 512]), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const gvoid*)src, (lvoid*)(dst + blk * 512), 16, 0, 0);
       }
       {
         const int r = pc / S::kCprV, c = (pc % S::kCprV) ^ swz<S::kCprV>(r);
         const uint16_t* src = vth + static_cast<size_t>(r) * np + kbase + c * 8;
-        __builtin_amdgcn_global_load_lds((const gvoid*)src, (lvoid*)(&vbuf[buf][blk * 512]), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds((const gvoid*)src, (lvoid*)(dst + S::kTile + blk * 512), 16, 0, 0);
       }
     }
   };
@@ -171,25 +181,12 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
   float m_run = -INFINITY;  // reference maximum, log2 units
   float l_part[4] = {0.f, 0.f, 0.f, 0.f};
 
-  if (NBUF == 2 && total > 0) {
-    issue(0, 0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
-  }
-  for (int u = 0; u < total; ++u) {
-    const int cur = NBUF == 2 ? (u & 1) : 0;
-    if (NBUF == 2) {
-      if (u + 1 < total) issue(u + 1, cur ^ 1);
-    } else {
-      __syncthreads();  // every wave is done with the buffers
-      issue(u, 0);
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();
-    }
+  // sub-tile u is computed from `cur` while sub-tile u+1 loads into `nxt`
+  auto step = [&](int u, const uint16_t* cur, uint16_t* nxt) {
+    if (u + 1 < total) issue(u + 1, nxt);
     const int valid = N - sub_base(u);  // real keys of this sub-tile (>= KS on all but the tail)
-    const char* kt = reinterpret_cast<const char*>(kbuf[cur]);
-    const char* vs = reinterpret_cast<const char*>(vbuf[cur]);
-
+    const char* kt = reinterpret_cast<const char*>(cur);
+    const char* vs = reinterpret_cast<const char*>(cur + S::kTile);
     f32x16 sacc[S::kKT];
 #pragma unroll
     for (int t = 0; t < S::kKT; ++t) {
@@ -246,10 +243,18 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
 #pragma unroll
       for (int w = 0; w < S::kKSK; ++w) oacc[dt] = mfma32(a[w], pb[w], oacc[dt]);
     }
-    if (NBUF == 2) {
-      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-      __syncthreads();  // next sub-tile landed; every wave is done with this one
-    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();  // sub-tile u+1 landed; every wave is done with sub-tile u
+  };
+
+  if (total > 0) {
+    issue(0, slot0);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __syncthreads();
+  }
+  for (int u = 0; u < total; u += 2) {
+    step(u, slot0, slot1);
+    if (u + 1 < total) step(u + 1, slot1, slot0);
   }
 
   const float l_run = (l_part[0] + l_part[1]) + (l_part[2] + l_part[3]);
@@ -351,8 +356,9 @@ hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const v
                          hipStream_t stream) {
   const float sl2 = p.scale * kLog2e;
   if (p.dtype == 0) {
-    // 64-key sub-tiles; double buffers when 128 query rows fill a workgroup
-    constexpr int kKs = 64, kNbuf = B == 128 ? 2 : 1;
+    // two LDS slots per workgroup: 64-key sub-tiles for 128-row blocks (64 KB,
+    // two workgroups per CU), 32-key sub-tiles for 64-row blocks (32 KB, four)
+    constexpr int kKs = B == 128 ? 64 : 32, kNbuf = 2;
     using S = AttnShape<D, B, kKs, kNbuf>;
     uint16_t* vt = static_cast<uint16_t*>(ws);
     hipLaunchKernelGGL((vt_kernel<D, B>), dim3(p.nb, p.heads), dim3(256), 0, stream,
