@@ -23,7 +23,15 @@
 namespace rsa {
 namespace {
 
-typedef __attribute__((address_space(1))) void gvoid;
+// Key sub-tile width and LDS ring depth of the 128-row bf16 kernel (kept
+// overridable at build time for tuning sweeps).
+#ifndef RSA_ATTN_KS
+#define RSA_ATTN_KS 32
+#endif
+#ifndef RSA_ATTN_NBUF
+#define RSA_ATTN_NBUF 4
+#endif
+
 typedef __attribute__((address_space(3))) void lvoid;
 
 // Position of `key` inside its 16-key group of V^T: the S^T result layout
@@ -99,13 +107,37 @@ __global__ __launch_bounds__(256) void vt_kernel(const uint16_t* __restrict__ v,
   }
 }
 
+// Workgroup barrier without the memory fence of __syncthreads(): the fence
+// would drain every outstanding direct-to-LDS prefetch.  The caller waits for
+// exactly the loads it needs (wait_vm); this wave's LDS reads are drained
+// first, so the slot they read may be refilled after the barrier.
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), no vmcnt / expcnt wait
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most `n` of this wave's vector-memory loads are in flight
+// (s_waitcnt with only the vmcnt field set; lgkmcnt 15 and expcnt 7 mean no
+// wait).  The builtin, unlike inline asm, is seen by the compiler's own wait
+// insertion, which then knows which direct-to-LDS loads have landed.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 // One workgroup per (head, query block): B/32 waves, 32 query rows each,
 // walking its key blocks in sub-tiles of KS keys.  K and V^T sub-tiles
-// stream global -> LDS directly (16-byte loads whose LDS destinations are
-// consecutive per wave; each lane picks the global chunk that belongs at its
-// slot of the swizzled layout).  NBUF = 2: the next sub-tile loads while the
-// current one is used.  Two or more workgroups share a CU, so one's softmax
-// (VALU) overlaps another's matrix products on every SIMD.
+// stream from HBM straight into a ring of NBUF LDS slots (buffer loads,
+// 16 bytes per lane, each lane fetching the chunk that belongs at its slot of
+// the swizzled layout).  Each wave software-pipelines its own work: the
+// matrix products for sub-tile j run next to the exponentials of sub-tile
+// j-1.  Two workgroups share a CU, so the two waves on every SIMD also
+// overlap each other's vector and matrix work.
 template <int D, int B, int KS, int NBUF>
 __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -113,13 +145,15 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
     const int* __restrict__ block_idx, uint16_t* __restrict__ out,
     float* __restrict__ lse, int H, int N, int NB, float scale_log2) {
   using S = AttnShape<D, B, KS, NBUF>;
-  static_assert(NBUF == 2, "two LDS slots");
-  // Slot arrays: K sub-tile at [0, kTile), V^T sub-tile after it.  Separate
+  static_assert(NBUF >= 3 && NBUF <= 4, "ring of 3 or 4 LDS slots");
+  // Ring slots: K sub-tile at [0, kTile), V^T sub-tile after it.  Separate
   // arrays, addressed with compile-time slot numbers, let the compiler see
   // that the slot being filled is not the one being read, so it does not
-  // drain the prefetch before the matrix products.
+  // drain the prefetches before the matrix products.
   __shared__ __attribute__((aligned(1024))) uint16_t slot0[2 * S::kTile];
   __shared__ __attribute__((aligned(1024))) uint16_t slot1[2 * S::kTile];
+  __shared__ __attribute__((aligned(1024))) uint16_t slot2[NBUF > 2 ? 2 * S::kTile : 8];
+  __shared__ __attribute__((aligned(1024))) uint16_t slot3[NBUF > 3 ? 2 * S::kTile : 8];
 
   // Head-synchronous schedule: workgroup ids go round-robin over the 8 XCDs;
   // XCD x takes the x-th contiguous eighth of the query blocks of one head
@@ -155,23 +189,38 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
   // first key and number of real keys of sub-tile u
   auto sub_base = [&](int u) { return list[u / S::kSub] * B + (u % S::kSub) * KS; };
 
+  // Tiles are fetched with buffer loads straight into LDS.  Each lane's byte
+  // offset inside a sub-tile is fixed for the whole loop, so only scalar
+  // registers change per sub-tile.  K: one buffer per sub-tile starting at
+  // its first key and ending at the last token, so rows past the end read as
+  // zeros (their scores are masked).  V^T: one buffer for the head's padded
+  // V^T, the sub-tile's first key added as the scalar offset.
+  constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
+  uint32_t koff[S::kLoads], voff[S::kLoads];
+#pragma unroll
+  for (int i = 0; i < S::kLoads; ++i) {
+    const int pc = (wave * S::kLoads + i) * 64 + lane;
+    const int kr = pc / S::kCprK;
+    koff[i] = static_cast<uint32_t>(kr * D + ((pc % S::kCprK) ^ swz<S::kCprK>(kr)) * 8) * 2u;
+    const int vr = pc / S::kCprV;
+    voff[i] = (static_cast<uint32_t>(vr) * static_cast<uint32_t>(np) +
+               static_cast<uint32_t>(((pc % S::kCprV) ^ swz<S::kCprV>(vr)) * 8)) * 2u;
+  }
+  const __amdgpu_buffer_rsrc_t vrsrc = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(vth), 0, static_cast<int>(D * np * 2), kRsrcWord3);
   auto issue = [&](int u, uint16_t* dst) {
     const int kbase = sub_base(u);
-    const int last = max(0, min(KS, N - kbase) - 1);
+    const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(kh + static_cast<size_t>(kbase) * D), 0, max(N - kbase, 0) * D * 2, kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
       const int blk = wave * S::kLoads + i;  // 1 KB block of the sub-tile
-      const int pc = blk * 64 + lane;        // physical 16-byte chunk
-      {
-        const int r = pc / S::kCprK, c = (pc % S::kCprK) ^ swz<S::kCprK>(r);
-        const uint16_t* src = kh + static_cast<size_t>(min(kbase + min(r, last), N - 1)) * D + c * 8;
-        __builtin_amdgcn_global_load_lds((const gvoid*)src, (lvoid*)(dst + blk * 512), 16, 0, 0);
-      }
-      {
-        const int r = pc / S::kCprV, c = (pc % S::kCprV) ^ swz<S::kCprV>(r);
-        const uint16_t* src = vth + static_cast<size_t>(r) * np + kbase + c * 8;
-        __builtin_amdgcn_global_load_lds((const gvoid*)src, (lvoid*)(dst + S::kTile + blk * 512), 16, 0, 0);
-      }
+      // (offsets passed as int: clang's host pass drops the kernel's launch
+      // stub when these arguments are unsigned array elements)
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(krsrc, (lvoid*)(dst + blk * 512), 16,
+                                               static_cast<int>(koff[i]), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(vrsrc, (lvoid*)(dst + S::kTile + blk * 512), 16,
+                                               static_cast<int>(voff[i]), kbase * 2, 0, 0);
     }
   };
 
@@ -181,24 +230,26 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
   float m_run = -INFINITY;  // reference maximum, log2 units
   float l_part[4] = {0.f, 0.f, 0.f, 0.f};
 
-  // sub-tile u is computed from `cur` while sub-tile u+1 loads into `nxt`
-  auto step = [&](int u, const uint16_t* cur, uint16_t* nxt) {
-    if (u + 1 < total) issue(u + 1, nxt);
-    const int valid = N - sub_base(u);  // real keys of this sub-tile (>= KS on all but the tail)
+  // S^T of one sub-tile (keys x this wave's queries) from the K slot `cur`
+  auto qk = [&](const uint16_t* cur, f32x16* sacc) {
     const char* kt = reinterpret_cast<const char*>(cur);
-    const char* vs = reinterpret_cast<const char*>(cur + S::kTile);
-    f32x16 sacc[S::kKT];
 #pragma unroll
-    for (int t = 0; t < S::kKT; ++t) {
-      const int r = 32 * t + col;
-      bf16x8 a[S::kKSD];
+    for (int t = 0; t < S::kKT; ++t) sacc[t] = f32x16{};
 #pragma unroll
-      for (int s = 0; s < S::kKSD; ++s)
-        a[s] = *reinterpret_cast<const bf16x8*>(kt + r * (2 * D) + (((2 * s + hl) ^ swz<S::kCprK>(r)) * 16));
-      sacc[t] = f32x16{};
+    for (int s = 0; s < S::kKSD; ++s) {
+      bf16x8 a[S::kKT];
 #pragma unroll
-      for (int s = 0; s < S::kKSD; ++s) sacc[t] = mfma32(a[s], qf[s], sacc[t]);
+      for (int t = 0; t < S::kKT; ++t) {
+        const int r = 32 * t + col;
+        a[t] = *reinterpret_cast<const bf16x8*>(kt + r * (2 * D) + (((2 * s + hl) ^ swz<S::kCprK>(r)) * 16));
+      }
+#pragma unroll
+      for (int t = 0; t < S::kKT; ++t) sacc[t] = mfma32(a[t], qf[s], sacc[t]);
     }
+  };
+  // keys at or past the last token (tail sub-tile only) get score -inf
+  auto mask_tail = [&](int u, f32x16* sacc) {
+    const int valid = N - sub_base(u);
     if (valid < KS) {
 #pragma unroll
       for (int t = 0; t < S::kKT; ++t)
@@ -206,16 +257,24 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
         for (int r = 0; r < 16; ++r)
           if (32 * t + acc_row(r, hl) >= valid) sacc[t][r] = -INFINITY;
     }
+  };
+  // maximum of this query's scores in the sub-tile, log2 units; the two
+  // lane halves hold different keys of the same query and swap once
+  auto rowmax = [&](const f32x16* sacc) {
     float mx = -INFINITY;
 #pragma unroll
     for (int t = 0; t < S::kKT; ++t)
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_blk = mx * scale_log2;
+    const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
+    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+  };
+  // lazy rescale: move the reference maximum only when the sub-tile's
+  // maximum exceeds it by more than 2^8
+  auto rescale = [&](float m_blk) {
     const bool need = m_blk > m_run + 8.f;
     const float m_use = need ? m_blk : m_run;
-    const float alpha = need ? exp2f(m_run - m_use) : 1.f;
+    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
     m_run = m_use;
 #pragma unroll
     for (int e = 0; e < 4; ++e) l_part[e] *= alpha;
@@ -223,12 +282,17 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
 #pragma unroll
       for (int t = 0; t < S::kDT; ++t) oacc[t] *= alpha;
     }
+  };
+  // P = 2^(S*scale - m) in bf16, row sums in fp32, then O^T += V^T P^T with
+  // V^T from the slot `cur`
+  auto pv = [&](const f32x16* sacc, const uint16_t* cur) {
+    const char* vs = reinterpret_cast<const char*>(cur + S::kTile);
     bf16x8 pb[S::kKSK];
 #pragma unroll
     for (int t = 0; t < S::kKT; ++t) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][r], scale_log2, -m_use));
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][r], scale_log2, -m_run));
         l_part[r & 3] += p;
         pb[2 * t + (r >> 3)][r & 7] = static_cast<__bf16>(p);
       }
@@ -243,18 +307,73 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
 #pragma unroll
       for (int w = 0; w < S::kKSK; ++w) oacc[dt] = mfma32(a[w], pb[w], oacc[dt]);
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();  // sub-tile u+1 landed; every wave is done with sub-tile u
   };
+  auto ring = [&](int i) { return i == 0 ? slot0 : i == 1 ? slot1 : i == 2 ? slot2 : slot3; };
 
+  // Sub-tile u lives in ring slot u % NBUF.  Software pipeline over the
+  // sub-tiles whose keys are all real: step j computes S^T of sub-tile j
+  // (matrix cores) next to the exponentials of sub-tile j-1 (VALU), then
+  // O += P V of sub-tile j-1.  Slots j-1 and j are read, the slot of j-2 is
+  // refilled with sub-tile j+NBUF-2, and NBUF-3 sub-tiles may still be in
+  // flight when step j waits for sub-tile j.
+  constexpr int kPer = 2 * S::kLoads;  // buffer loads per lane per sub-tile
+  f32x16 sprev[S::kKT];
+  float mprev = -INFINITY;
+  // leading sub-tiles with no key past the last token: only the last listed
+  // block can be the ragged block NB-1
+  int total_full = total;
   if (total > 0) {
-    issue(0, slot0);
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __syncthreads();
+    const int last = list[cnt - 1];
+    if (last == NB - 1) total_full = total - S::kSub + min(S::kSub, (N - last * B) / KS);
   }
-  for (int u = 0; u < total; u += 2) {
-    step(u, slot0, slot1);
-    if (u + 1 < total) step(u + 1, slot1, slot0);
+  int next = min(NBUF - 2, total);  // first sub-tile not yet requested
+  for (int i = 0; i < NBUF - 2 && i < total; ++i) issue(i, ring(i));
+  int j = 0;
+  bool pending = false;  // sprev holds sub-tile j-1, not yet in O
+  if (total_full >= NBUF + 1 && total >= 2 * NBUF - 2) {
+    wait_vm<(NBUF - 3) * kPer>();
+    barrier_lds();
+    issue(NBUF - 2, ring(NBUF - 2));
+    qk(slot0, sprev);
+    mprev = rowmax(sprev);
+    j = 1;
+    pending = true;
+    auto step = [&](const uint16_t* kslot, const uint16_t* vslot, uint16_t* fill, int jj) {
+      rescale(mprev);
+      wait_vm<(NBUF - 3) * kPer>();
+      barrier_lds();
+      issue(jj + NBUF - 2, fill);
+      f32x16 scur[S::kKT];
+      qk(kslot, scur);
+      pv(sprev, vslot);
+#pragma unroll
+      for (int t = 0; t < S::kKT; ++t) sprev[t] = scur[t];
+      mprev = rowmax(sprev);
+    };
+    // groups of NBUF steps starting at j = 1 mod NBUF: compile-time slots
+    while (j + NBUF - 1 < total_full && j + 2 * NBUF - 3 < total) {
+      step(ring(1 % NBUF), slot0, ring((NBUF - 1) % NBUF), j);
+      step(ring(2 % NBUF), ring(1 % NBUF), slot0, j + 1);
+      if constexpr (NBUF > 2) step(ring(3 % NBUF), ring(2 % NBUF), ring(1 % NBUF), j + 2);
+      if constexpr (NBUF > 3) step(slot0, ring(3 % NBUF), ring(2 % NBUF), j + 3);
+      j += NBUF;
+    }
+    next = j + NBUF - 2;
+  }
+  if (pending) {  // finish sub-tile j-1
+    rescale(mprev);
+    pv(sprev, ring((j - 1) % NBUF));
+  }
+  // the rest, one sub-tile per step with full waits (ragged tail included)
+  for (; j < total; ++j) {
+    wait_vm<0>();
+    barrier_lds();
+    for (; next < total && next <= j + NBUF - 1; ++next) issue(next, ring(next % NBUF));
+    f32x16 sc[S::kKT];
+    qk(ring(j % NBUF), sc);
+    mask_tail(j, sc);
+    rescale(rowmax(sc));
+    pv(sc, ring(j % NBUF));
   }
 
   const float l_run = (l_part[0] + l_part[1]) + (l_part[2] + l_part[3]);
@@ -356,9 +475,9 @@ hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const v
                          hipStream_t stream) {
   const float sl2 = p.scale * kLog2e;
   if (p.dtype == 0) {
-    // two LDS slots per workgroup: 64-key sub-tiles for 128-row blocks (64 KB,
-    // two workgroups per CU), 32-key sub-tiles for 64-row blocks (32 KB, four)
-    constexpr int kKs = B == 128 ? 64 : 32, kNbuf = 2;
+    // 64 KB of LDS per 128-row workgroup (two per CU): a ring of four 32-key
+    // sub-tiles; 48 KB per 64-row workgroup: three 32-key slots
+    constexpr int kKs = RSA_ATTN_KS, kNbuf = B == 128 ? RSA_ATTN_NBUF : 3;
     using S = AttnShape<D, B, kKs, kNbuf>;
     uint16_t* vt = static_cast<uint16_t*>(ws);
     hipLaunchKernelGGL((vt_kernel<D, B>), dim3(p.nb, p.heads), dim3(256), 0, stream,
