@@ -1,9 +1,12 @@
-// Block-sparse attention over a compacted key-block list (gfx950).
+// Block-sparse attention over compacted key-block lists (gfx950).
 //
 // PARK (Accurate Block Retrieval for Sparse Attention in Video Diffusion
 // Transformers), Abstract: attention is computed only inside the retrieved
 // key blocks.  Query i of block I sees the tokens of the key blocks listed
-// for (h, I); the softmax is normalised over exactly those tokens.
+// for (h, I); the softmax is normalised over exactly those tokens (a block
+// listed twice counts once, the order of a list does not matter).  A first
+// kernel rewrites every list in canonical form (ascending, no repeats, no
+// invalid entries); the attention kernels walk the canonical lists.
 //
 // bf16 kernel, one workgroup per (head, query block), one wave per 32 query
 // rows.  Everything is computed transposed so that a lane owns one query:
@@ -54,6 +57,51 @@ __device__ __forceinline__ int swz(int r) {
   if constexpr (CPR == 16) return r & 15;
   else if constexpr (CPR == 8) return (r >> 1) & 7;
   else return (r >> 2) & 3;
+}
+
+constexpr int kMaxNB = 4096;  // largest number of blocks per sequence
+
+// Canonical lists.  One workgroup per (query block I, head h): marks the
+// listed blocks in an LDS byte map and compacts the map in ascending order
+// into clist[h, I, 0..ccount[h, I]).  The count is clamped to [0, NB] and
+// indices outside [0, NB) are dropped.
+__global__ __launch_bounds__(256) void canon_kernel(const int* __restrict__ counts,
+                                                    const int* __restrict__ block_idx,
+                                                    int* __restrict__ ccount, int* __restrict__ clist,
+                                                    int NB) {
+  __shared__ uint8_t mark[kMaxNB];
+  __shared__ int wsum[4];
+  const int I = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const size_t row = static_cast<size_t>(h) * NB + I;
+  for (int e = tid; e < NB; e += 256) mark[e] = 0;
+  __syncthreads();
+  const int c = min(max(counts[row], 0), NB);
+  for (int t = tid; t < c; t += 256) {
+    const int j = block_idx[row * NB + t];
+    if (static_cast<unsigned>(j) < static_cast<unsigned>(NB)) mark[j] = 1;  // repeats write the same byte
+  }
+  __syncthreads();
+  int* out = clist + row * NB;
+  int base = 0;
+  for (int r0 = 0; r0 < NB; r0 += 256) {
+    const int e = r0 + tid;
+    const bool f = e < NB && mark[e] != 0;
+    const uint64_t bal = __ballot(f);
+    const int pre = __builtin_popcountll(bal & ((1ull << lane) - 1));
+    if (lane == 0) wsum[wave] = __builtin_popcountll(bal);
+    __syncthreads();
+    int off = base, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      off += w < wave ? wsum[w] : 0;
+      tot += wsum[w];
+    }
+    if (f) out[off + pre] = e;
+    base += tot;
+    __syncthreads();
+  }
+  if (tid == 0) ccount[row] = base;
 }
 
 // Work of one workgroup: B/32 waves (32 query rows each) against key
@@ -141,8 +189,8 @@ __device__ __forceinline__ void wait_vm() {
 template <int D, int B, int KS, int NBUF>
 __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
-    const uint16_t* __restrict__ vt, const int* __restrict__ counts,
-    const int* __restrict__ block_idx, uint16_t* __restrict__ out,
+    const uint16_t* __restrict__ vt, const int* __restrict__ ccount,
+    const int* __restrict__ clist, uint16_t* __restrict__ out,
     float* __restrict__ lse, int H, int N, int NB, float scale_log2) {
   using S = AttnShape<D, B, KS, NBUF>;
   static_assert(NBUF >= 3 && NBUF <= 4, "ring of 3 or 4 LDS slots");
@@ -180,9 +228,9 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
     }
   }
 
-  const int cnt = counts[h * NB + I];
+  const int cnt = ccount[h * NB + I];
   const int total = cnt * S::kSub;  // sub-tiles to visit
-  const int* list = block_idx + (static_cast<size_t>(h) * NB + I) * NB;
+  const int* list = clist + (static_cast<size_t>(h) * NB + I) * NB;
   const uint16_t* kh = k + head_off;
   const uint16_t* vth = vt + static_cast<size_t>(h) * D * np;
 
@@ -319,8 +367,8 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
   constexpr int kPer = 2 * S::kLoads;  // buffer loads per lane per sub-tile
   f32x16 sprev[S::kKT];
   float mprev = -INFINITY;
-  // leading sub-tiles with no key past the last token: only the last listed
-  // block can be the ragged block NB-1
+  // leading sub-tiles with no key past the last token: the canonical list is
+  // ascending, so only its last entry can be the ragged block NB-1
   int total_full = total;
   if (total > 0) {
     const int last = list[cnt - 1];
@@ -397,12 +445,12 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
 }
 
 // fp32 inputs: plain fp32 arithmetic, one thread per query row, K and V
-// staged in LDS 32 keys at a time and read as broadcasts.  Same online
-// softmax (exact rescaling at every chunk).
+// staged in LDS 32 keys at a time and read as broadcasts, over the canonical
+// list.  Same online softmax (exact rescaling at every chunk).
 template <int D, int B>
 __global__ __launch_bounds__(B) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
-    const int* __restrict__ counts, const int* __restrict__ block_idx,
+    const int* __restrict__ ccount, const int* __restrict__ clist,
     float* __restrict__ out, float* __restrict__ lse, int N, int NB, float scale_log2) {
   constexpr int kChunk = 32;
   __shared__ float Ks[kChunk * D];
@@ -419,8 +467,8 @@ __global__ __launch_bounds__(B) void attn_f32_kernel(
     o[d] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
-  const int cnt = counts[h * NB + I];
-  const int* list = block_idx + (static_cast<size_t>(h) * NB + I) * NB;
+  const int cnt = ccount[h * NB + I];
+  const int* list = clist + (static_cast<size_t>(h) * NB + I) * NB;
   for (int it = 0; it < cnt; ++it) {
     const int kbase = list[it] * B;
     const int bJ = min(B, N - kbase);
@@ -469,29 +517,52 @@ __global__ __launch_bounds__(B) void attn_f32_kernel(
   }
 }
 
+// Attention workspace: [V^T (bf16 only)][canonical counts][canonical lists],
+// each part 256-byte aligned.
+struct AttnWs {
+  size_t ccount_off, clist_off, total;
+};
+
+AttnWs attn_ws_layout(const Problem& p) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  const size_t rows = static_cast<size_t>(p.heads) * p.nb;
+  AttnWs w;
+  w.ccount_off = p.dtype == 0 ? al(sizeof(uint16_t) * p.heads * p.head_dim * static_cast<size_t>(p.nb) * p.block) : 0;
+  w.clist_off = w.ccount_off + al(sizeof(int) * rows);
+  w.total = w.clist_off + al(sizeof(int) * rows * p.nb);
+  return w;
+}
+
 template <int D, int B>
 hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const void* v,
                          const int* counts, const int* idx, void* out, float* lse, void* ws,
                          hipStream_t stream) {
   const float sl2 = p.scale * kLog2e;
+  const AttnWs w = attn_ws_layout(p);
+  char* base = static_cast<char*>(ws);
+  int* ccount = reinterpret_cast<int*>(base + w.ccount_off);
+  int* clist = reinterpret_cast<int*>(base + w.clist_off);
+  hipLaunchKernelGGL(canon_kernel, dim3(p.nb, p.heads), dim3(256), 0, stream, counts, idx, ccount, clist, p.nb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   if (p.dtype == 0) {
     // 64 KB of LDS per 128-row workgroup (two per CU): a ring of four 32-key
     // sub-tiles; 48 KB per 64-row workgroup: three 32-key slots
     constexpr int kKs = RSA_ATTN_KS, kNbuf = B == 128 ? RSA_ATTN_NBUF : 3;
     using S = AttnShape<D, B, kKs, kNbuf>;
-    uint16_t* vt = static_cast<uint16_t*>(ws);
+    uint16_t* vt = reinterpret_cast<uint16_t*>(base);
     hipLaunchKernelGGL((vt_kernel<D, B>), dim3(p.nb, p.heads), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(v), vt, p.tokens, p.nb);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int grid = 8 * ((p.nb + 7) / 8) * p.heads;
     hipLaunchKernelGGL((attn_bf16_kernel<D, B, kKs, kNbuf>), dim3(grid), dim3(S::kThreads), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt, counts,
-                       idx, static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2);
+                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt, ccount,
+                       clist, static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2);
   } else {
     hipLaunchKernelGGL((attn_f32_kernel<D, B>), dim3(p.heads * p.nb), dim3(B), 0, stream,
                        static_cast<const float*>(q), static_cast<const float*>(k),
-                       static_cast<const float*>(v), counts, idx, static_cast<float*>(out),
+                       static_cast<const float*>(v), ccount, clist, static_cast<float*>(out),
                        lse, p.tokens, p.nb, sl2);
   }
   return hipGetLastError();
@@ -499,10 +570,7 @@ hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const v
 
 }  // namespace
 
-size_t attn_ws_bytes(const Problem& p) {
-  if (p.dtype != 0) return 0;
-  return (sizeof(uint16_t) * p.heads * p.head_dim * static_cast<size_t>(p.nb) * p.block + 255) / 256 * 256;
-}
+size_t attn_ws_bytes(const Problem& p) { return attn_ws_layout(p).total; }
 
 hipError_t launch_attention(const Problem& p, const void* q, const void* k, const void* v,
                             const int* counts, const int* idx, void* out, float* lse, void* ws,

@@ -192,18 +192,22 @@ rsa_status rsa_mask_drift(const rsa_problem* p, const void* q, const void* k,
  *   lse[h,i]   = log sum_t exp(scale * <q_i, k_t>)   (natural log).
  *
  * q, k, v: [heads, tokens, head_dim] of `dtype`, 16-byte aligned.
- * counts: [heads, NB] int32, each in [0, NB]; block_idx: [heads, NB, NB]
- *   int32, entries in [0, NB) (e.g. the output of rsa_select_topp, fresh or
- *   cached).  A row with count 0 gives out = 0 and lse = -inf.
+ * counts: [heads, NB] int32; block_idx: [heads, NB, NB] int32 (e.g. the
+ *   output of rsa_select_topp, fresh or cached).  Row (h, I) lists the key
+ *   blocks block_idx[h,I,0..counts[h,I]) in any order; a block listed twice
+ *   counts once, counts are clamped to [0, NB] and entries outside [0, NB)
+ *   are ignored.  A row with no valid entry gives out = 0 and lse = -inf.
  * out: [heads, tokens, head_dim] of `dtype` (bf16 rounded to nearest even).
  * lse: [heads, tokens] fp32 output or NULL.
  * bf16 inputs: bf16 matrix-core products with fp32 accumulation and an fp32
  *   online softmax; fp32 inputs: fp32 arithmetic throughout.
  * ws / ws_bytes: at least rsa_workspace_bytes(p, RSA_OP_ATTN) bytes, 256-byte
- *   aligned (bf16: heads * head_dim * NB * block * 2 bytes, where v is
- *   re-laid out key-major for the matrix cores; fp32: 0, may be NULL / 0).
- * Out-of-range counts or indices are not checked on the device: the caller
- * guarantees them (rsa_select_topp's outputs always satisfy them).
+ *   aligned, each part rounded up to 256 bytes: (bf16 only) v re-laid out
+ *   key-major for the matrix cores, heads * head_dim * NB * block * 2 bytes;
+ *   then every row's list in canonical form (ascending, no repeats, no
+ *   invalid entries): counts, heads * NB * 4 bytes, and lists,
+ *   heads * NB * NB * 4 bytes.
+ * Non-finite values in q, k or v give undefined results.
  */
 rsa_status rsa_block_sparse_attn(const rsa_problem* p, const void* q, const void* k,
                                  const void* v, const int32_t* counts,

@@ -62,8 +62,11 @@ def test_workspace_sizes():
     assert B.workspace_bytes(p, B.OP_SCORE) == want
     assert B.workspace_bytes(p, B.OP_DRIFT) == 8 * 2 * 64 * 40
     assert B.workspace_bytes(p, B.OP_SELECT) == 0
-    assert B.workspace_bytes(p, B.OP_ATTN) == 2 * 40 * 128 * 591 * 128        # v re-laid out key-major
-    assert B.workspace_bytes(prob(heads=40, grid=(21, 45, 80), b=128, dtype=1), B.OP_ATTN) == 0
+    # attention: v re-laid out key-major (bf16), then the canonical list
+    # counts and lists of every row
+    lists = al(4 * 40 * 591) + al(4 * 40 * 591 * 591)
+    assert B.workspace_bytes(p, B.OP_ATTN) == al(2 * 40 * 128 * 591 * 128) + lists
+    assert B.workspace_bytes(prob(heads=40, grid=(21, 45, 80), b=128, dtype=1), B.OP_ATTN) == lists
     assert B.workspace_bytes(prob(d=96), B.OP_SCORE) == 0          # invalid problem -> 0
 
 

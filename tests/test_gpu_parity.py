@@ -160,6 +160,50 @@ def test_attention_matches_oracle_on_gpu_lists(name):
     assert worst[0] <= tol_l2 and worst[1] <= tol_abs and worst[2] <= tol_lse
 
 
+@pytest.mark.parametrize("name", ["bf16_d128_b128", "bf16_d64_b64", "fp32_d128_b128"])
+def test_attention_lists_are_sets(name):
+    """A row's list may come in any order, repeat blocks, hold entries
+    outside [0, NB) and carry a count above NB: the visible keys are the set
+    of valid listed blocks (oracle: token mask of that set), so the result
+    equals the one on the sorted, duplicate-free lists bit for bit."""
+    r = run(name)
+    wl = r.wl
+    nb = wl.nblocks
+    counts, idx = host(r.counts), host(r.idx)
+    rng = np.random.default_rng(7)
+    c2 = counts.copy()
+    i2 = np.zeros_like(idx)
+    for h in range(wl.heads):
+        for i in range(nb):
+            sel = idx[h, i, :counts[h, i]]
+            extra = list(rng.choice(sel, size=min(2, nb - len(sel)), replace=True)) if len(sel) else []
+            if len(sel) + len(extra) < nb:
+                extra.append(-3 if i % 2 else nb + 4)          # dropped entries
+            row = np.concatenate([sel, np.asarray(extra, dtype=sel.dtype)])
+            rng.shuffle(row)
+            c2[h, i] = len(row)
+            i2[h, i, :len(row)] = row
+    # one row lists every block in reverse with a count above NB
+    c2[0, 0] = nb + 3
+    i2[0, 0] = np.arange(nb)[::-1]
+    out, lse = R.block_sparse_attn(r.q, r.k, r.v, dev(torch.from_numpy(c2)), dev(torch.from_numpy(i2)), r.p)
+    torch.cuda.synchronize()
+    o_ref, l_ref = r.out, r.lse
+    # row (0, 0) now sees every block: the oracle gives its reference
+    o00, l00 = O.block_sparse_attention(r.q64[0], r.k64[0], r.v64[0], wl.block, [list(range(nb))],
+                                        query_blocks=[0])
+    out_h, lse_h = host(out.float()).astype(np.float64), host(lse).astype(np.float64)
+    b = wl.block
+    same = torch.equal(out[:, b:], o_ref[:, b:]) and torch.equal(out[1:], o_ref[1:])
+    same_l = torch.equal(lse[:, b:], l_ref[:, b:]) and torch.equal(lse[1:], l_ref[1:])
+    tol_l2, tol_abs, tol_lse = ATTN_TOL[wl.dtype]
+    e = (rel_l2(out_h[0, :b], o00), np.abs(out_h[0, :b] - o00).max(), np.abs(lse_h[0, :b] - l00).max())
+    say(f"[gpu] {name}: set-semantics rows bit-identical {same and same_l}; "
+        f"all-blocks row rel-L2 {e[0]:.2e} max-abs {e[1]:.2e} lse {e[2]:.2e}")
+    assert same and same_l
+    assert e[0] <= tol_l2 and e[1] <= tol_abs and e[2] <= tol_lse
+
+
 @pytest.mark.parametrize("name", ["bf16_d128_b128", "bf16_d64_b64", "fp32_tiny"])
 def test_drift_and_refresh_match_oracle(name):
     r = run(name)
