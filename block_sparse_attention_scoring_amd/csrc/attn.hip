@@ -35,8 +35,6 @@ namespace {
 #define RSA_ATTN_NBUF 4
 #endif
 
-typedef __attribute__((address_space(3))) void lvoid;
-
 // Position of `key` inside its 16-key group of V^T: the S^T result layout
 // gives lane half h keys {4h..4h+3, 8+4h..8+4h+3}, so groups 1 and 2 of
 // four keys are swapped.
@@ -46,18 +44,6 @@ __host__ __device__ __forceinline__ int vt_pos(int key) {
   return (key & ~15) | (sw << 2) | (key & 3);
 }
 
-// XOR swizzle of the 16-byte chunks of an LDS tile row holding `cpr` chunks:
-// 16 consecutive rows read at one logical chunk hit 16 distinct bank groups.
-// Bank group of (row r, physical chunk p) is (r * CPR + p) mod 16; XOR-ing the
-// logical chunk with the row bits above the rows sharing 256 bytes makes the
-// 16 rows of one read distinct.
-template <int CPR>
-__device__ __forceinline__ int swz(int r) {
-  static_assert(CPR == 4 || CPR == 8 || CPR == 16, "swizzle defined for rows of 4, 8 or 16 chunks");
-  if constexpr (CPR == 16) return r & 15;
-  else if constexpr (CPR == 8) return (r >> 1) & 7;
-  else return (r >> 2) & 3;
-}
 
 constexpr int kMaxNB = 4096;  // largest number of blocks per sequence
 
@@ -155,28 +141,6 @@ __global__ __launch_bounds__(256) void vt_kernel(const uint16_t* __restrict__ v,
   }
 }
 
-// Workgroup barrier without the memory fence of __syncthreads(): the fence
-// would drain every outstanding direct-to-LDS prefetch.  The caller waits for
-// exactly the loads it needs (wait_vm); this wave's LDS reads are drained
-// first, so the slot they read may be refilled after the barrier.
-// The empty asm statements keep the compiler from moving memory accesses
-// across the barrier.
-__device__ __forceinline__ void barrier_lds() {
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), no vmcnt / expcnt wait
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Wait until at most `n` of this wave's vector-memory loads are in flight
-// (s_waitcnt with only the vmcnt field set; lgkmcnt 15 and expcnt 7 mean no
-// wait).  The builtin, unlike inline asm, is seen by the compiler's own wait
-// insertion, which then knows which direct-to-LDS loads have landed.
-template <int n>
-__device__ __forceinline__ void wait_vm() {
-  static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
-  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // One workgroup per (head, query block): B/32 waves, 32 query rows each,
 // walking its key blocks in sub-tiles of KS keys.  K and V^T sub-tiles
@@ -243,7 +207,6 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
   // its first key and ending at the last token, so rows past the end read as
   // zeros (their scores are masked).  V^T: one buffer for the head's padded
   // V^T, the sub-tile's first key added as the scalar offset.
-  constexpr int kRsrcWord3 = 0x00020000;  // raw buffer, 32-bit data format
   uint32_t koff[S::kLoads], voff[S::kLoads];
 #pragma unroll
   for (int i = 0; i < S::kLoads; ++i) {

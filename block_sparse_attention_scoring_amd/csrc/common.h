@@ -62,4 +62,47 @@ __device__ __forceinline__ float wave_max(float v) {
   return v;
 }
 
+
+typedef __attribute__((address_space(3))) void lvoid;
+
+// Word 3 of a raw buffer resource (stride 0, 32-bit data format): loads past
+// the record count return zeros.
+constexpr int kRsrcWord3 = 0x00020000;
+
+// XOR swizzle of the 16-byte chunks of an LDS tile row holding `cpr` chunks:
+// 16 consecutive rows read at one logical chunk hit 16 distinct bank groups.
+// Bank group of (row r, physical chunk p) is (r * CPR + p) mod 16; XOR-ing the
+// logical chunk with the row bits above the rows sharing 256 bytes makes the
+// 16 rows of one read distinct.
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+  static_assert(CPR == 4 || CPR == 8 || CPR == 16, "swizzle defined for rows of 4, 8 or 16 chunks");
+  if constexpr (CPR == 16) return r & 15;
+  else if constexpr (CPR == 8) return (r >> 1) & 7;
+  else return (r >> 2) & 3;
+}
+
+// Workgroup barrier without the memory fence of __syncthreads(): the fence
+// would drain every outstanding direct-to-LDS prefetch.  The caller waits for
+// exactly the loads it needs (wait_vm); this wave's LDS reads are drained
+// first, so the slot they read may be refilled after the barrier.
+// The empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
+__device__ __forceinline__ void barrier_lds() {
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0), no vmcnt / expcnt wait
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+// Wait until at most `n` of this wave's vector-memory loads are in flight
+// (s_waitcnt with only the vmcnt field set; lgkmcnt 15 and expcnt 7 mean no
+// wait).  The builtin, unlike inline asm, is seen by the compiler's own wait
+// insertion, which then knows which direct-to-LDS loads have landed.
+template <int n>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt is 6 bits");
+  __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 }  // namespace rsa

@@ -19,6 +19,8 @@ that definition:
   Temporal Mask Reuse (HEART abstract; HASTE abstract).
 * ``trajectory``- estimate once, cache, reuse, refresh on drift (RAPID
   abstract; HEART abstract), plus RAPID's Turbo re-selection on cached scores.
+* ``retrieval`` - block retrieval accuracy: each query block's dense attention
+  mass per key block, and the mass a selection captures (PARK, Abstract).
 
 What pins each function (closed forms, invariants, brute force, independent
 library routines) is in ``tests/test_oracle.py``; no function here is left
@@ -30,10 +32,11 @@ from .selection import select_row, select_topp, density
 from .attention import block_sparse_attention, token_mask
 from .drift import drift, refresh_decision
 from .trajectory import cache_trajectory, turbo_schedule
+from .retrieval import captured_mass, dense_block_mass
 
 __all__ = [
     "block_bounds", "num_blocks", "pool_keys", "score_blocks", "score_head",
     "score_blocks_pooled_query", "select_row", "select_topp", "density",
     "block_sparse_attention", "token_mask", "drift", "refresh_decision",
-    "cache_trajectory", "turbo_schedule",
+    "cache_trajectory", "turbo_schedule", "dense_block_mass", "captured_mass",
 ]

@@ -385,3 +385,69 @@ def test_turbo_decaying_p_is_nested_and_density_non_increasing():
     for (m_prev, c_prev), (m, c) in zip(stages, stages[1:]):
         assert (m <= m_prev).all()
         assert (O.density(c, 30) <= O.density(c_prev, 30)).all()
+
+
+# ---------------------------------------------------------------- retrieval accuracy
+
+@pytest.mark.parametrize("n,b,d", [(96, 16, 8), (100, 16, 8), (37, 8, 5)])
+def test_dense_block_mass_equals_sdpa_with_block_indicator_values(n, b, d):
+    """Dense block mass against torch SDPA over all tokens with one-hot block
+    values (ragged last block included): a wrong softmax axis, a missing
+    scale, a divisor of B for the ragged query block or summing over the
+    wrong axis all fail here."""
+    q, k = _rand((n, d), 41, 2.0), _rand((n, d), 42, 2.0)
+    nb = O.num_blocks(n, b)
+    owner = np.arange(n) // b
+    indicator = np.eye(nb)[owner]                              # [n, nb]
+    per_query = _sdpa(q, k, indicator, scale=0.7)              # [n, nb] dense mass per block
+    want = np.stack([per_query[i * b:min(n, i * b + b)].mean(axis=0) for i in range(nb)])
+    got = O.dense_block_mass(q, k, b, scale=0.7)
+    np.testing.assert_allclose(got, want, atol=1e-13)
+    np.testing.assert_allclose(got.sum(axis=1), 1.0, atol=1e-13)
+    np.testing.assert_allclose(O.dense_block_mass(q, k, b, scale=0.7, query_blocks=[nb - 1, 0]),
+                               got[[nb - 1, 0]], atol=0)
+
+
+def test_dense_block_mass_brute_force_tiny():
+    n, b, d = 10, 4, 3                                         # blocks of 4, 4, 2 tokens
+    q, k = _rand((n, d), 43), _rand((n, d), 44)
+    s = 1 / math.sqrt(d)
+    nb = 3
+    want = np.zeros((nb, nb))
+    for I in range(nb):
+        rows = range(I * b, min(n, I * b + b))
+        for i in rows:
+            w = [math.exp(s * sum(q[i, x] * k[t, x] for x in range(d))) for t in range(n)]
+            z = sum(w)
+            for t in range(n):
+                want[I, t // b] += w[t] / z / len(rows)
+    np.testing.assert_allclose(O.dense_block_mass(q, k, b), want, atol=1e-14)
+
+
+def test_dense_block_mass_closed_forms():
+    n, b, d = 100, 16, 8
+    k = _rand((n, d), 45)
+    # zero queries: uniform attention, mass proportional to block sizes
+    sizes = np.array([16] * 6 + [4], float)
+    np.testing.assert_allclose(O.dense_block_mass(np.zeros((n, d)), k, b),
+                               np.tile(sizes / n, (7, 1)), atol=1e-15)
+    # one block: all mass on it
+    np.testing.assert_allclose(O.dense_block_mass(_rand((12, d), 46), _rand((12, d), 47), 16), [[1.0]], atol=1e-15)
+
+
+def test_dense_block_mass_equals_park_scores_for_blockwise_constant_keys():
+    """Keys constant within each block and B | N: PARK's per-query block
+    softmax is exactly the dense mass (two independent codes agree)."""
+    n, b, d = 128, 16, 8
+    nb = n // b
+    k = np.repeat(_rand((nb, d), 48, 1.5), b, axis=0)
+    q = _rand((n, d), 49, 2.0)
+    np.testing.assert_allclose(O.dense_block_mass(q, k, b), O.score_head(q, k, b, 1 / math.sqrt(d)),
+                               atol=1e-13)
+
+
+def test_captured_mass():
+    m = np.array([[0.5, 0.25, 0.25], [0.1, 0.2, 0.7], [1 / 3, 1 / 3, 1 / 3]])
+    assert O.captured_mass(m, [[0], [2], []]) == pytest.approx((0.5 + 0.7 + 0.0) / 3, abs=1e-15)
+    assert O.captured_mass(m, [[0, 1, 2]] * 3) == pytest.approx(1.0, abs=1e-15)
+    assert O.captured_mass(m, [[1, 2], [0, 1], [2]]) == pytest.approx((0.5 + 0.3 + 1 / 3) / 3, abs=1e-15)
