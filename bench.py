@@ -45,6 +45,8 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
+    ap.add_argument("--retrieval", action="store_true",
+                    help="report block retrieval accuracy (dense mass captured at equal density) instead")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -150,6 +152,87 @@ def copy_probe(mib):
     print(json.dumps({"copy_probe_bytes": n, "launches": 3}))
 
 
+def retrieval(args):
+    """Block retrieval accuracy on one workload (PARK, Abstract).
+
+    The dense attention mass of each query block per key block (exact, from
+    rsa_dense_block_mass) is the yardstick.  PARK's scores select by top-p;
+    at the same number of blocks per row the query-pooled comparison scorer
+    and the ideal choice (top blocks by dense mass) are measured too, and the
+    pooled scorer's own top-p selection is reported with its density.  The
+    analysis of the library's outputs runs on the host with NumPy.
+    """
+    import numpy as np
+    import torch
+    import workloads as W
+    import block_sparse_attention_scoring_amd as R
+
+    wl = W.CONFIGS[args.workload]
+    inp = W.make_inputs(wl)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q, k = inp.q.to(dev), inp.k.to(dev)
+    p = R.make_problem(q, wl.grid, wl.block)
+    top_p = torch.from_numpy(inp.top_p).to(dev)
+    stream = torch.cuda.current_stream(dev)
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            out = fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return out, e0.elapsed_time(e1) / reps
+
+    S, t_park = timed(lambda: R.score_blocks(q, k, p))
+    Sp, t_pool = timed(lambda: R.score_blocks_pooled(q, k, p))
+    M, t_mass = timed(lambda: R.dense_block_mass(q, k, p))
+    _, counts, _, dens = R.select_topp(S, top_p, p)
+    _, counts_p, _, dens_p = R.select_topp(Sp, top_p, p)
+    torch.cuda.synchronize()
+    S, Sp, M = S.cpu().numpy(), Sp.cpu().numpy(), M.cpu().numpy().astype(np.float64)
+    kk, kp = counts.cpu().numpy(), counts_p.cpu().numpy()
+
+    def take(scores, kcount):
+        # the kcount best blocks per row (score descending, lower index first)
+        order = np.argsort(-scores, axis=-1, kind="stable")
+        rank = np.empty_like(order)
+        np.put_along_axis(rank, order, np.arange(scores.shape[-1])[None, None, :].repeat(
+            scores.shape[0], 0).repeat(scores.shape[1], 1), axis=-1)
+        return rank < kcount[..., None]
+
+    sel_park, sel_pool_k = take(S, kk), take(Sp, kk)
+    sel_ideal, sel_pool_p = take(M, kk), take(Sp, kp)
+    cap = lambda sel: float((M * sel).sum(-1).mean())
+    recall = lambda sel: float((sel & sel_ideal).sum() / sel_ideal.sum())
+    nb = wl.nblocks
+    dense_flops = 2 * 2.0 * wl.tokens * wl.tokens * wl.head_dim * wl.heads
+    res = {
+        "mode": "retrieval",
+        "metric": "dense attention mass captured by the selected key blocks (mean over query blocks)",
+        "workload": wl.name, "heads": wl.heads, "tokens": wl.tokens, "block": wl.block,
+        "top_p": float(inp.top_p[0]),
+        "data": "synthetic (seeded smooth 3-D field + noise; no weights)",
+        "equal_density": {
+            "density": round(float(kk.sum() / (wl.heads * nb * nb)), 4),
+            "park_top_p": round(cap(sel_park), 4),
+            "pooled_query_same_count": round(cap(sel_pool_k), 4),
+            "ideal_same_count": round(cap(sel_ideal), 4),
+            "recall_of_ideal_blocks": {"park": round(recall(sel_park), 4),
+                                       "pooled_query": round(recall(sel_pool_k), 4)},
+        },
+        "pooled_query_top_p": {"density": round(float(kp.sum() / (wl.heads * nb * nb)), 4),
+                               "captured": round(cap(sel_pool_p), 4)},
+        "ms": {"park_scores": round(t_park, 3), "pooled_scores": round(t_pool, 3),
+               "dense_block_mass": round(t_mass, 3)},
+        "dense_block_mass_tflops": round(dense_flops / (t_mass * 1e-3) / 1e12, 1),
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -159,6 +242,9 @@ def main():
         sys.exit(2)
     if args.copy_probe:
         copy_probe(args.copy_probe)
+        return
+    if args.retrieval:
+        retrieval(args)
         return
 
     import numpy as np

@@ -2,16 +2,20 @@
 
 The hot path is four library calls (include/rsa.h): PARK block scoring,
 top-p selection, the per-head drift check of Temporal Mask Reuse and
-block-sparse flash attention.  This package is only their ctypes binding
-plus the host loop that reuses cached masks across denoising steps.
+block-sparse flash attention.  Two more calls measure block retrieval
+accuracy (dense block mass, query-pooled comparison scores).  This package is
+only their ctypes binding plus the host loop that reuses cached masks across
+denoising steps.
 """
 from .binding import (Problem, RsaError, RsaLibraryMissing, block_sparse_attn, declared_functions,
-                      lib, make_problem, mask_drift, score_blocks, select_topp, workspace_bytes,
-                      OP_ATTN, OP_DRIFT, OP_SCORE, OP_SELECT, RSA_BF16, RSA_FP32, LIB_PATH)
+                      dense_block_mass, lib, make_problem, mask_drift, score_blocks,
+                      score_blocks_pooled, select_topp, workspace_bytes, OP_ATTN, OP_DRIFT,
+                      OP_POOLED, OP_SCORE, OP_SELECT, RSA_BF16, RSA_FP32, LIB_PATH)
 from .cache import MaskCache
 
 __all__ = [
-    "Problem", "RsaError", "RsaLibraryMissing", "block_sparse_attn", "declared_functions", "lib",
-    "make_problem", "mask_drift", "score_blocks", "select_topp", "workspace_bytes", "MaskCache",
-    "OP_ATTN", "OP_DRIFT", "OP_SCORE", "OP_SELECT", "RSA_BF16", "RSA_FP32", "LIB_PATH",
+    "Problem", "RsaError", "RsaLibraryMissing", "block_sparse_attn", "declared_functions",
+    "dense_block_mass", "lib", "make_problem", "mask_drift", "score_blocks", "score_blocks_pooled",
+    "select_topp", "workspace_bytes", "MaskCache", "OP_ATTN", "OP_DRIFT", "OP_POOLED", "OP_SCORE",
+    "OP_SELECT", "RSA_BF16", "RSA_FP32", "LIB_PATH",
 ]

@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "lib", "librsa.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "rsa.h")
 
 RSA_BF16, RSA_FP32 = 0, 1
-OP_SCORE, OP_SELECT, OP_DRIFT, OP_ATTN = 0, 1, 2, 3
+OP_SCORE, OP_SELECT, OP_DRIFT, OP_ATTN, OP_POOLED = 0, 1, 2, 3, 4
 
 
 class RsaLibraryMissing(RuntimeError):
@@ -71,6 +71,8 @@ def _declare(lib):
         "rsa_select_topp": (i32, [pp, _P, _P, i32, _P, _P, _P, _P, _P, _P, sz, _P]),
         "rsa_mask_drift": (i32, [pp, _P, _P, _P, _P, f32, i32, _P, _P, _P, sz, _P]),
         "rsa_block_sparse_attn": (i32, [pp, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
+        "rsa_dense_block_mass": (i32, [pp, _P, _P, _P, _P]),
+        "rsa_score_blocks_pooled": (i32, [pp, _P, _P, _P, _P, sz, _P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -193,3 +195,24 @@ def block_sparse_attn(q, k, v, counts, block_idx, p: Problem, out=None, lse=None
                                        _ptr(block_idx), _ptr(out), _ptr(lse), _ptr(ws), wsb,
                                        _stream(q)), "rsa_block_sparse_attn")
     return out, lse
+
+
+def dense_block_mass(q, k, p: Problem, out=None):
+    """Dense attention mass of each query block per key block [heads, NB, NB] fp32."""
+    nb = p.nblocks
+    if out is None:
+        out = torch.empty((p.heads, nb, nb), dtype=torch.float32, device=q.device)
+    _check(lib().rsa_dense_block_mass(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(out), _stream(q)),
+           "rsa_dense_block_mass")
+    return out
+
+
+def score_blocks_pooled(q, k, p: Problem, out=None, workspace=None):
+    """Query-pooled comparison scores [heads, NB, NB] fp32 (rsa_score_blocks_pooled)."""
+    nb = p.nblocks
+    if out is None:
+        out = torch.empty((p.heads, nb, nb), dtype=torch.float32, device=q.device)
+    ws, wsb = _workspace(p, OP_POOLED, q.device, workspace)
+    _check(lib().rsa_score_blocks_pooled(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(out), _ptr(ws), wsb,
+                                         _stream(q)), "rsa_score_blocks_pooled")
+    return out

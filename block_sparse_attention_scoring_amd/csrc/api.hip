@@ -45,6 +45,7 @@ size_t ws_bytes_for(const rsa::Problem& p, int op) {
     case RSA_OP_SCORE: return rsa::score_ws_layout(p, nullptr, nullptr);
     case RSA_OP_DRIFT: return rsa::drift_ws_bytes(p);
     case RSA_OP_ATTN: return rsa::attn_ws_bytes(p);
+    case RSA_OP_POOLED: return rsa::pooled_ws_bytes(p);
     default: return 0;
   }
 }
@@ -148,3 +149,25 @@ rsa_status rsa_block_sparse_attn(const rsa_problem* p, const void* q, const void
 }
 
 }  // extern "C"
+
+rsa_status rsa_dense_block_mass(const rsa_problem* p, const void* q, const void* k, float* mass,
+                                hipStream_t stream) {
+  rsa::Problem pr;
+  rsa_status st = make_problem(p, &pr);
+  if (st != RSA_OK) return st;
+  if (q == nullptr || k == nullptr || mass == nullptr) return RSA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(mass)) return RSA_ERR_ALIGN;
+  return hip_status(rsa::launch_dense_mass(pr, q, k, mass, stream));
+}
+
+rsa_status rsa_score_blocks_pooled(const rsa_problem* p, const void* q, const void* k,
+                                   float* pooled, void* ws, size_t ws_bytes, hipStream_t stream) {
+  rsa::Problem pr;
+  rsa_status st = make_problem(p, &pr);
+  if (st != RSA_OK) return st;
+  if (q == nullptr || k == nullptr || pooled == nullptr) return RSA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(pooled)) return RSA_ERR_ALIGN;
+  st = check_ws(pr, RSA_OP_POOLED, ws, ws_bytes);
+  if (st != RSA_OK) return st;
+  return hip_status(rsa::launch_pooled_scores(pr, q, k, pooled, ws, stream));
+}

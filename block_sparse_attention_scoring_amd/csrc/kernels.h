@@ -45,4 +45,16 @@ hipError_t launch_attention(const Problem& p, const void* q, const void* k, cons
                             const int* counts, const int* idx, void* out, float* lse, void* ws,
                             hipStream_t stream);
 
+// Block means of x [H, N, D] times `mul`, written as fp32 [H, NB, D] (the
+// scoring pool kernel; bmax gets each block's max |.|).
+hipError_t launch_block_means(const Problem& p, const void* x, double mul, float* out, float* bmax,
+                              hipStream_t stream);
+// Retrieval accuracy: dense block mass (no workspace) and the query-pooled
+// comparison scorer (workspace: pooled q and k, block maxima).
+hipError_t launch_dense_mass(const Problem& p, const void* q, const void* k, float* mass,
+                             hipStream_t stream);
+size_t pooled_ws_bytes(const Problem& p);
+hipError_t launch_pooled_scores(const Problem& p, const void* q, const void* k, float* scores,
+                                void* ws, hipStream_t stream);
+
 }  // namespace rsa

@@ -390,6 +390,26 @@ hipError_t launch_scoring_t(const Problem& p, const void* q, const void* k,
 
 }  // namespace
 
+hipError_t launch_block_means(const Problem& p, const void* x, double mul, float* out, float* bmax,
+                              hipStream_t stream) {
+  if (p.dtype == 0) {
+    if (p.head_dim == 128)
+      hipLaunchKernelGGL((pool_kernel<uint16_t, 128>), dim3(p.nb, p.heads), dim3(kPoolThreads), 0, stream,
+                         static_cast<const uint16_t*>(x), nullptr, out, bmax, p.tokens, p.nb, p.block, mul);
+    else
+      hipLaunchKernelGGL((pool_kernel<uint16_t, 64>), dim3(p.nb, p.heads), dim3(kPoolThreads), 0, stream,
+                         static_cast<const uint16_t*>(x), nullptr, out, bmax, p.tokens, p.nb, p.block, mul);
+  } else {
+    if (p.head_dim == 128)
+      hipLaunchKernelGGL((pool_kernel<float, 128>), dim3(p.nb, p.heads), dim3(kPoolThreads), 0, stream,
+                         static_cast<const float*>(x), nullptr, out, bmax, p.tokens, p.nb, p.block, mul);
+    else
+      hipLaunchKernelGGL((pool_kernel<float, 64>), dim3(p.nb, p.heads), dim3(kPoolThreads), 0, stream,
+                         static_cast<const float*>(x), nullptr, out, bmax, p.tokens, p.nb, p.block, mul);
+  }
+  return hipGetLastError();
+}
+
 size_t score_ws_layout(const Problem& p, ScoreWs* ws, void* base) {
   const size_t NBp = (p.nb + kScoreRowPad - 1) / kScoreRowPad * kScoreRowPad;
   auto align = [](size_t x) { return (x + 255) / 256 * 256; };

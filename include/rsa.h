@@ -24,6 +24,11 @@
  *   rsa_block_sparse_attn attention computed only inside the retrieved key
  *                         blocks (PARK, Abstract).
  *
+ * Two more calls measure block retrieval accuracy, PARK's stated goal
+ * (Abstract): rsa_dense_block_mass gives each query block's exact dense
+ * attention mass per key block, and rsa_score_blocks_pooled the comparison
+ * scorer that averages the queries before the softmax.
+ *
  * Common conventions
  * ------------------
  * Tensors q, k, v, out are [heads, tokens, head_dim], row-major, tokens in
@@ -73,7 +78,13 @@ typedef enum {
   RSA_ERR_ARG = 7        /* a scalar argument is out of range (e.g. NaN threshold) */
 } rsa_status;
 
-typedef enum { RSA_OP_SCORE = 0, RSA_OP_SELECT = 1, RSA_OP_DRIFT = 2, RSA_OP_ATTN = 3 } rsa_op;
+typedef enum {
+  RSA_OP_SCORE = 0,
+  RSA_OP_SELECT = 1,
+  RSA_OP_DRIFT = 2,
+  RSA_OP_ATTN = 3,
+  RSA_OP_POOLED = 4 /* rsa_score_blocks_pooled */
+} rsa_op;
 
 /*
  * Problem descriptor (host struct, read during the call only).
@@ -213,6 +224,39 @@ rsa_status rsa_block_sparse_attn(const rsa_problem* p, const void* q, const void
                                  const void* v, const int32_t* counts,
                                  const int32_t* block_idx, void* out, float* lse,
                                  void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Dense block mass: the retrieval-accuracy yardstick (PARK, Abstract: block
+ * retrieval accuracy).  For query block I of head h, with the softmax taken
+ * over all N keys,
+ *
+ *   mass[h,I,J] = (1/b_I) sum_{i in I} sum_{t in J} softmax_t(scale * <q_i, k_t>),
+ *
+ * the mean over I's queries of the attention mass on key block J; every row
+ * sums to 1.  q, k: [heads, tokens, head_dim] of `dtype`, 16-byte aligned.
+ * mass: [heads, NB, NB] fp32, 16-byte aligned.  No workspace.  Costs two
+ * dense Q K^T passes (bf16 matrix cores, fp32 exponentials, fp64 row
+ * normalisers); meant for measurement, not for the sparse step.
+ */
+rsa_status rsa_dense_block_mass(const rsa_problem* p, const void* q, const void* k, float* mass,
+                                hipStream_t stream);
+
+/*
+ * Query-pooled block scores: the scorer PARK's abstract argues against
+ * (averaging a block's queries before the softmax loses their individual
+ * preferences), kept as the comparison for retrieval accuracy:
+ *
+ *   pooled[h,I,J] = softmax_J(scale * <qbar_I, kbar_J>),
+ *
+ * qbar_I and kbar_J the block means (over the tokens each block holds).
+ * Rows sum to 1.  q, k as in rsa_score_blocks; pooled: [heads, NB, NB] fp32.
+ * ws / ws_bytes: at least rsa_workspace_bytes(p, RSA_OP_POOLED) bytes,
+ * 256-byte aligned (pooled q and k, [heads, NB, head_dim] fp32 each, and a
+ * block-maximum scratch).  Block means are fp64 sums rounded once to fp32;
+ * logits and the softmax are fp64.
+ */
+rsa_status rsa_score_blocks_pooled(const rsa_problem* p, const void* q, const void* k,
+                                   float* pooled, void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

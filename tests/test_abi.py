@@ -41,7 +41,8 @@ class Buf:
 def test_exports_every_declared_symbol(lib):
     names = R.declared_functions()
     assert set(names) == {"rsa_workspace_bytes", "rsa_status_str", "rsa_version", "rsa_score_blocks",
-                          "rsa_select_topp", "rsa_mask_drift", "rsa_block_sparse_attn"}
+                          "rsa_select_topp", "rsa_mask_drift", "rsa_block_sparse_attn",
+                          "rsa_dense_block_mass", "rsa_score_blocks_pooled"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -67,6 +68,8 @@ def test_workspace_sizes():
     lists = al(4 * 40 * 591) + al(4 * 40 * 591 * 591)
     assert B.workspace_bytes(p, B.OP_ATTN) == al(2 * 40 * 128 * 591 * 128) + lists
     assert B.workspace_bytes(prob(heads=40, grid=(21, 45, 80), b=128, dtype=1), B.OP_ATTN) == lists
+    # query-pooled scorer: pooled q and k, then block maxima
+    assert B.workspace_bytes(p, B.OP_POOLED) == 2 * al(4 * 40 * 591 * 128) + al(4 * 40 * 591)
     assert B.workspace_bytes(prob(d=96), B.OP_SCORE) == 0          # invalid problem -> 0
 
 
@@ -106,6 +109,9 @@ def test_null_problem_and_pointers(lib):
                               b.ptr, 1 << 30, None) == NULL
     assert lib.rsa_block_sparse_attn(ctypes.byref(p), b.ptr, b.ptr, None, b.ptr, b.ptr, b.ptr, None,
                                      None, 0, None) == NULL
+    assert lib.rsa_dense_block_mass(ctypes.byref(p), b.ptr, b.ptr, None, None) == NULL
+    assert lib.rsa_dense_block_mass(None, b.ptr, b.ptr, b.ptr, None) == NULL
+    assert lib.rsa_score_blocks_pooled(ctypes.byref(p), b.ptr, None, b.ptr, b.ptr, 1 << 30, None) == NULL
     assert b.untouched()
 
 
@@ -116,6 +122,8 @@ def test_alignment(lib):
     assert lib.rsa_block_sparse_attn(ctypes.byref(p), mis, b.ptr, b.ptr, b.ptr, b.ptr, b.ptr, None,
                                      b.ptr, 1 << 30, None) == ALIGN
     assert lib.rsa_score_blocks(ctypes.byref(p), b.ptr, b.ptr, None, mis, b.ptr, 1 << 30, None) == ALIGN
+    assert lib.rsa_dense_block_mass(ctypes.byref(p), b.ptr, mis, b.ptr, None) == ALIGN
+    assert lib.rsa_score_blocks_pooled(ctypes.byref(p), b.ptr, b.ptr, mis, b.ptr, 1 << 30, None) == ALIGN
     assert b.untouched()
 
 
@@ -130,6 +138,9 @@ def test_workspace_checks(lib):
     aneed = B.workspace_bytes(p, B.OP_ATTN)
     assert lib.rsa_block_sparse_attn(ctypes.byref(p), b.ptr, b.ptr, b.ptr, b.ptr, b.ptr, b.ptr, None,
                                      b.ptr, aneed - 1, None) == WS
+    pneed = B.workspace_bytes(p, B.OP_POOLED)
+    assert lib.rsa_score_blocks_pooled(ctypes.byref(p), b.ptr, b.ptr, b.ptr, b.ptr, pneed - 1, None) == WS
+    assert lib.rsa_score_blocks_pooled(ctypes.byref(p), b.ptr, b.ptr, b.ptr, None, pneed, None) == WS
     dneed = B.workspace_bytes(p, B.OP_DRIFT)
     assert lib.rsa_mask_drift(ctypes.byref(p), b.ptr, b.ptr, b.ptr, b.ptr, 0.05, 1, b.ptr, b.ptr,
                               b.ptr, dneed - 8, None) == WS
