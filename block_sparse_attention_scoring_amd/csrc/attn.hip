@@ -175,7 +175,8 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
   const int h = slot / per_xcd, I = xcd * per_xcd + slot % per_xcd;
   if (h >= H || I >= NB) return;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS addresses stay scalar
   const int hl = lane >> 5, col = lane & 31;
   const size_t head_off = static_cast<size_t>(h) * N * D;
   const size_t np = static_cast<size_t>(NB) * B;
@@ -284,12 +285,12 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
   // maximum exceeds it by more than 2^8
   auto rescale = [&](float m_blk) {
     const bool need = m_blk > m_run + 8.f;
-    const float m_use = need ? m_blk : m_run;
-    const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
-    m_run = m_use;
+    if (__any(need)) {  // rare: skip the factor's exponential otherwise
+      const float m_use = need ? m_blk : m_run;
+      const float alpha = need ? __builtin_amdgcn_exp2f(m_run - m_use) : 1.f;
+      m_run = m_use;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) l_part[e] *= alpha;
-    if (__any(need)) {
+      for (int e = 0; e < 4; ++e) l_part[e] *= alpha;
 #pragma unroll
       for (int t = 0; t < S::kDT; ++t) oacc[t] *= alpha;
     }
