@@ -18,6 +18,8 @@
 //          recomputes the logits, forms the per-query softmax and sums it
 //          over the query block in a fixed order.  No atomics: the result is
 //          bitwise reproducible.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -174,191 +176,250 @@ __device__ __forceinline__ float reduce_scatter_32(const float (&v)[16], int col
   return d + swap_lanes<1>(d);
 }
 
-template <typename T, int D, int B>
-struct ScoreShape {
-  static constexpr bool kSplitQ = sizeof(T) == 4;  // fp32 queries: two fp16 terms
-  static constexpr int kSub = B / 32;              // 32-row query sub-tiles
-  static constexpr int kKS = D / 16;               // k-steps over head_dim
-  static constexpr int kQStride = D + 8;           // LDS pitch (fp16), 16 B pad
-  static constexpr int kLanesPerRow = D / 8;
-  static constexpr int kRowsPerPass = kScoreThreads / kLanesPerRow;
-};
+// One workgroup per (head, query block), one wave per 32 query rows.  Each
+// wave keeps its rows in registers, scaled by the row's own power of two and
+// held as fp16 (exact for bf16 input; fp32 input adds a second fp16 term).
+// The split pooled keys stream in chunks of 32 key blocks (hi and lo tiles)
+// into a ring of NBUF LDS slots with buffer loads, shared by all waves.
+// Both passes form one walk of 2 x NBp/32 chunk steps, so the prefetch runs
+// on across the pass boundary:
+//   pass 1 (chunk steps 0..nc-1): logits S^T = Kbar Q^T (hi and lo terms in
+//     two accumulation chains), per-query running max and normaliser; the
+//     two lane halves hold different key blocks of the same query and merge
+//     once at the end of the pass;
+//   pass 2 (steps nc..2nc-1): the logits again, untransposed this time
+//     (S = Q Kbar^T: the same registers and LDS reads with the operands
+//     swapped), so a lane holds one key block for 16 of the wave's queries
+//     and the softmax summed over queries is 16 in-lane additions and one
+//     exchange between the lane halves; each query's scale, maximum and
+//     weight 1/(b_I * normaliser) enter as per-register constants (the
+//     weight folded into the exponent).  The waves' partial sums of a chunk
+//     meet in an LDS pair (indexed by chunk parity) and are added in wave
+//     order after the next step's barrier.
+// Store to LDS outside the compiler's wait tracking.  Its own wait insertion
+// cannot tell this store from a write into the ring slots the direct-to-LDS
+// loads fill, so it would drain them first; the target never overlaps a slot
+// and the next barrier_lds() waits for the store (lgkmcnt).
+__device__ __forceinline__ void lds_store_f32(float* p, float v) {
+  const uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lvoid*)p));
+  asm volatile("ds_write_b32 %0, %1" ::"v"(a), "v"(v) : "memory");
+}
 
-template <typename T, int D, int B>
-__global__ __launch_bounds__(kScoreThreads, 2) void score_kernel(
+template <typename T, int D, int B, int NBUF>
+__global__ __launch_bounds__(2 * B, 2) void score_kernel(
     const T* __restrict__ q, const _Float16* __restrict__ khi, const _Float16* __restrict__ klo,
     const float* __restrict__ inv_t, const uint8_t* __restrict__ head_active,
     float* __restrict__ scores, int N, int NB, int NBp) {
-  using S = ScoreShape<T, D, B>;
-  __shared__ __attribute__((aligned(16))) _Float16 Qh[B * S::kQStride];
-  __shared__ __attribute__((aligned(16))) _Float16 Ql[S::kSplitQ ? B * S::kQStride : 8];
-  __shared__ float row_inv[B];
-  __shared__ float part_m[kScoreWaves * 2][B];
-  __shared__ float part_z[kScoreWaves * 2][B];
-  __shared__ float row_m[B];
-  __shared__ float row_w[B];
+  constexpr bool kSplitQ = sizeof(T) == 4;
+  constexpr int kWaves = B / 32, kThreads = kWaves * kWave;
+  constexpr int kKS = D / 16;                              // k-steps over head_dim
+  constexpr int kTile = 32 * D;                            // fp16 elements of a hi (or lo) tile
+  constexpr int kCpr = D / 8;                              // 16-byte chunks per row
+  constexpr int kLoads = kTile * 2 / 16 / kThreads;        // loads per lane per tile
+  constexpr int kPer = 2 * kLoads;                         // loads per lane per step
+  static_assert(kLoads >= 1 && kTile * 2 % (16 * kThreads) == 0, "tile not divisible");
+  static_assert(NBUF >= 2 && NBUF <= 4, "ring of 2 to 4 LDS slots");
+  __shared__ __attribute__((aligned(1024))) _Float16 slot0[2 * kTile];
+  __shared__ __attribute__((aligned(1024))) _Float16 slot1[2 * kTile];
+  __shared__ __attribute__((aligned(1024))) _Float16 slot2[NBUF > 2 ? 2 * kTile : 8];
+  __shared__ __attribute__((aligned(1024))) _Float16 slot3[NBUF > 3 ? 2 * kTile : 8];
+  __shared__ float part[2][kWaves][32];
+  __shared__ float qconst[kWaves][2][32];  // per query of a wave: scale, -max - log2(weight)
 
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int h = tile / NB, I = tile - h * NB;
   if (head_active != nullptr && head_active[h] == 0) return;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, col = lane & 31;
   const int q0 = I * B, bI = min(B, N - q0);
+  const bool qvalid = wave * 32 + col < bI;
 
-  // ---- queries -> per-row power-of-two scale -> fp16 in LDS
+  // ---- this lane's query values (row wave*32+col, columns 16s+8hl..+7)
+  f16x8 qh[kKS], ql[kSplitQ ? kKS : 1];
+  float sc;
   {
-    const int rg = tid / S::kLanesPerRow, c8 = tid % S::kLanesPerRow;
-    for (int r = rg; r < B; r += S::kRowsPerPass) {
-      float x[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-      if (r < bI) load8<T>(q + (static_cast<size_t>(h) * N + q0 + r) * D + c8 * 8, x);
-      float a = 0.f;
+    float x[kKS][8];
+    // rows past the last token read row q0 and are zeroed
+    const T* src = q + (static_cast<size_t>(h) * N + q0 + (qvalid ? wave * 32 + col : 0)) * D + 8 * hl;
+    const float keep = qvalid ? 1.f : 0.f;
+    float a = 0.f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(x[e]));
-#pragma unroll
-      for (int o = 1; o < S::kLanesPerRow; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
-      const int sh = scale_shift(a);
-      const float s = pow2i(sh);
-      f16x8 hi, lo;
+    for (int s = 0; s < kKS; ++s) {
+      load8<T>(src + 16 * s, x[s]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float xs = x[e] * s;
-        hi[e] = static_cast<_Float16>(xs);
-        lo[e] = static_cast<_Float16>(xs - static_cast<float>(hi[e]));
+        x[s][e] *= keep;
+        a = fmaxf(a, fabsf(x[s][e]));
       }
-      *reinterpret_cast<f16x8*>(&Qh[r * S::kQStride + c8 * 8]) = hi;
-      if constexpr (S::kSplitQ) *reinterpret_cast<f16x8*>(&Ql[r * S::kQStride + c8 * 8]) = lo;
-      if (c8 == 0) row_inv[r] = pow2i(-sh);
     }
-  }
-  __syncthreads();
-
-  const float it_h = inv_t[h];
-  float sc[S::kSub];
+    a = fmaxf(a, __shfl_xor(a, 32));  // the other half of the row
+    const int sh = scale_shift(a);
+    const float sf = pow2i(sh);
 #pragma unroll
-  for (int st = 0; st < S::kSub; ++st) sc[st] = row_inv[32 * st + col] * it_h;
+    for (int s = 0; s < kKS; ++s) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const float xs = x[s][e] * sf;
+        qh[s][e] = static_cast<_Float16>(xs);
+        if constexpr (kSplitQ) ql[s][e] = static_cast<_Float16>(xs - static_cast<float>(qh[s][e]));
+      }
+    }
+    sc = pow2i(-sh) * inv_t[h];
+  }
 
-  const int n_chunks = NBp / 32;
+  // ---- chunk loads: pooled-key rows 32c..32c+31, hi then lo
+  const int nc = NBp / 32;
+  const int U = 2 * nc;  // steps: pass 1 then pass 2
   const _Float16* kh_head = khi + static_cast<size_t>(h) * NBp * D;
   const _Float16* kl_head = klo + static_cast<size_t>(h) * NBp * D;
+  uint32_t off[kLoads];
+#pragma unroll
+  for (int i = 0; i < kLoads; ++i) {
+    const int pc = (wave * kLoads + i) * 64 + lane;
+    const int r = pc / kCpr;
+    off[i] = static_cast<uint32_t>(r * D + ((pc % kCpr) ^ swz<kCpr>(r)) * 8) * 2u;
+  }
+  auto issue = [&](int u, _Float16* dst) __attribute__((always_inline)) {
+    const int c = u < nc ? u : u - nc;
+    const size_t base = static_cast<size_t>(32 * c) * D;
+    const __amdgpu_buffer_rsrc_t rh =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(kh_head + base), 0, kTile * 2, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rl =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(kl_head + base), 0, kTile * 2, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int blk = wave * kLoads + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lvoid*)(dst + blk * 512), 16, static_cast<int>(off[i]), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lvoid*)(dst + kTile + blk * 512), 16, static_cast<int>(off[i]), 0,
+                                               0, 0);
+    }
+  };
 
-  // logits of chunk c (32 key blocks) for query sub-tile st, raw units; the
-  // hi and lo terms run as two independent accumulation chains
-  auto logits = [&](const f16x8 (&ahi)[S::kKS], const f16x8 (&alo)[S::kKS], int st) {
+  // ---- logits of one chunk, raw units (rows past NB: -inf)
+  // kTr: S^T (lane = query, registers = key blocks) for pass 1, else S
+  // (lane = key block, registers = queries) for pass 2
+  auto logits = [&](int c, const _Float16* cur, auto kTr) __attribute__((always_inline)) {
+    const char* th = reinterpret_cast<const char*>(cur);
+    const char* tl = reinterpret_cast<const char*>(cur + kTile);
     f32x16 acc_hi = f32x16{}, acc_lo = f32x16{};
 #pragma unroll
-    for (int s = 0; s < S::kKS; ++s) {
-      const f16x8 b = *reinterpret_cast<const f16x8*>(&Qh[(32 * st + col) * S::kQStride + 16 * s + 8 * hl]);
-      acc_hi = mfma32(ahi[s], b, acc_hi);
-      acc_lo = mfma32(alo[s], b, acc_lo);
-      if constexpr (S::kSplitQ) {
-        const f16x8 bl = *reinterpret_cast<const f16x8*>(&Ql[(32 * st + col) * S::kQStride + 16 * s + 8 * hl]);
-        acc_lo = mfma32(ahi[s], bl, acc_lo);
+    for (int s = 0; s < kKS; ++s) {
+      const int o = col * (2 * D) + (((2 * s + hl) ^ swz<kCpr>(col)) * 16);
+      const f16x8 ah = *reinterpret_cast<const f16x8*>(th + o);
+      const f16x8 al = *reinterpret_cast<const f16x8*>(tl + o);
+      if constexpr (decltype(kTr)::value) {
+        acc_hi = mfma32(ah, qh[s], acc_hi);
+        acc_lo = mfma32(al, qh[s], acc_lo);
+        if constexpr (kSplitQ) acc_lo = mfma32(ah, ql[s], acc_lo);
+      } else {
+        acc_hi = mfma32(qh[s], ah, acc_hi);
+        acc_lo = mfma32(qh[s], al, acc_lo);
+        if constexpr (kSplitQ) acc_lo = mfma32(ql[s], ah, acc_lo);
       }
     }
     return acc_hi + acc_lo;
   };
-  auto load_a = [&](int c, f16x8 (&ahi)[S::kKS], f16x8 (&alo)[S::kKS]) {
-    const size_t row = static_cast<size_t>(32 * c + col) * D + 8 * hl;
+
+  float mraw = -INFINITY, z = 0.f;  // pass 1, this half's key blocks
+  float qs[16], qm[16];              // pass 2: per register (query) constants
+  float* srow = scores + (static_cast<size_t>(h) * NB + I) * NB;
+  // all waves' partial sums of chunk c are in part[c & 1]
+  auto finish = [&](int c) __attribute__((always_inline)) {
+    if (wave == 0 && lane < 32 && 32 * c + lane < NB) {
+      float t = 0.f;
 #pragma unroll
-    for (int s = 0; s < S::kKS; ++s) {
-      ahi[s] = *reinterpret_cast<const f16x8*>(kh_head + row + 16 * s);
-      alo[s] = *reinterpret_cast<const f16x8*>(kl_head + row + 16 * s);
+      for (int w = 0; w < kWaves; ++w) t += part[c & 1][w][lane];
+      srow[32 * c + lane] = t;
     }
   };
-
-  // ---- pass 1: per-query max and normaliser over all key blocks
-  float mraw[S::kSub], z[S::kSub];
-#pragma unroll
-  for (int st = 0; st < S::kSub; ++st) {
-    mraw[st] = -INFINITY;
-    z[st] = 0.f;
-  }
-  for (int c = wave; c < n_chunks; c += kScoreWaves) {
-    f16x8 ahi[S::kKS], alo[S::kKS];
-    load_a(c, ahi, alo);
-    const bool tail = 32 * c + 32 > NB;
-#pragma unroll
-    for (int st = 0; st < S::kSub; ++st) {
-      __builtin_amdgcn_sched_barrier(0);  // one sub-tile's registers live at a time
-      f32x16 acc = logits(ahi, alo, st);
-      if (tail) {
+  auto body = [&](int u, const _Float16* cur) __attribute__((always_inline)) {
+    if (u < nc) {
+      f32x16 acc = logits(u, cur, std::true_type{});
+      if (32 * u + 32 > NB) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          if (32 * c + acc_row(r, hl) >= NB) acc[r] = -INFINITY;
+          if (32 * u + acc_row(r, hl) >= NB) acc[r] = -INFINITY;
       }
       float cm = -INFINITY;
 #pragma unroll
       for (int r = 0; r < 16; ++r) cm = fmaxf(cm, acc[r]);
-      if (cm > mraw[st]) {
-        z[st] *= exp2f((mraw[st] - cm) * sc[st]);
-        mraw[st] = cm;
+      if (cm > mraw) {
+        z *= exp2f((mraw - cm) * sc);
+        mraw = cm;
       }
-      if (mraw[st] > -INFINITY) {
-        const float mb = -mraw[st] * sc[st];
-        float zs = 0.f;
+      if (mraw > -INFINITY) {
+        const float mb = -mraw * sc;
+        float zs[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int r = 0; r < 16; ++r) zs += __builtin_amdgcn_exp2f(fmaf(acc[r], sc[st], mb));
-        z[st] += zs;
+        for (int r = 0; r < 16; ++r) zs[r & 3] += __builtin_amdgcn_exp2f(fmaf(acc[r], sc, mb));
+        z += (zs[0] + zs[1]) + (zs[2] + zs[3]);
       }
+      if (u == nc - 1) {
+        // merge the two halves' statistics of each query; hand every lane the
+        // constants of the 16 queries its registers hold in pass 2
+        const float ml = mraw > -INFINITY ? mraw * sc : -INFINITY;
+        const float mo = __shfl_xor(ml, 32), zo = __shfl_xor(z, 32);
+        const float m = fmaxf(ml, mo);
+        const float zt = (ml > -INFINITY ? z * exp2f(ml - m) : 0.f) + (mo > -INFINITY ? zo * exp2f(mo - m) : 0.f);
+        // p / (b_I zt) = 2^(s*sc - m - log2(b_I zt)); rows past the end get
+        // +inf, so their terms are exactly 0
+        const float mw = qvalid ? m + log2f(static_cast<float>(bI) * zt) : INFINITY;
+        if (hl == 0) {
+          lds_store_f32(&qconst[wave][0][col], sc);
+          lds_store_f32(&qconst[wave][1][col], mw);
+        }
+        __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's stores (lgkmcnt(0))
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          qs[r] = qconst[wave][0][acc_row(r, hl)];
+          qm[r] = -qconst[wave][1][acc_row(r, hl)];
+        }
+      }
+      return;
     }
-  }
+    const int c = u - nc;
+    if (c > 0) finish(c - 1);
+    const f32x16 acc = logits(c, cur, std::false_type{});
+    // key block 32c + col of this lane; the registers hold 16 queries
+    float ps[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int st = 0; st < S::kSub; ++st) {
-    part_m[wave * 2 + hl][32 * st + col] = mraw[st] > -INFINITY ? mraw[st] * sc[st] : -INFINITY;
-    part_z[wave * 2 + hl][32 * st + col] = z[st];
+    for (int r = 0; r < 16; ++r) ps[r & 3] += __builtin_amdgcn_exp2f(fmaf(acc[r], qs[r], qm[r]));
+    float t = (ps[0] + ps[1]) + (ps[2] + ps[3]);
+    t += __shfl_xor(t, 32);  // the other 16 queries
+    if (hl == 0) lds_store_f32(&part[c & 1][wave][col], t);
+  };
+
+  // ---- the walk: ring slot u % NBUF, NBUF-1 chunks in flight
+  auto ring = [&](int i) { return i == 0 ? slot0 : i == 1 ? slot1 : i == 2 ? slot2 : slot3; };
+  auto steady = [&](int u, const _Float16* cur, _Float16* nxt) __attribute__((always_inline)) {
+    wait_vm<(NBUF - 2) * kPer>();
+    barrier_lds();
+    issue(u + NBUF - 1, nxt);
+    body(u, cur);
+  };
+  int u = 0;
+  if (U >= 2 * NBUF - 1) {
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) issue(i, ring(i));
+    do {
+      steady(u, slot0, ring(NBUF - 1));
+      steady(u + 1, slot1, slot0);
+      if constexpr (NBUF > 2) steady(u + 2, slot2, slot1);
+      if constexpr (NBUF > 3) steady(u + 3, slot3, slot2);
+      u += NBUF;
+    } while (u + 2 * NBUF - 2 < U);
+  } else {
+    for (int i = 0; i < NBUF - 1 && i < U; ++i) issue(i, ring(i));
+  }
+  for (; u < U; ++u) {
+    wait_vm<0>();
+    barrier_lds();
+    if (u + NBUF - 1 < U) issue(u + NBUF - 1, ring((u + NBUF - 1) % NBUF));
+    body(u, ring(u % NBUF));
   }
   __syncthreads();
-  if (tid < B) {
-    float m = -INFINITY;
-#pragma unroll
-    for (int g = 0; g < kScoreWaves * 2; ++g) m = fmaxf(m, part_m[g][tid]);
-    float zt = 0.f;
-#pragma unroll
-    for (int g = 0; g < kScoreWaves * 2; ++g)
-      if (part_m[g][tid] > -INFINITY) zt += part_z[g][tid] * exp2f(part_m[g][tid] - m);
-    row_m[tid] = m;
-    row_w[tid] = tid < bI ? 1.f / (static_cast<float>(bI) * zt) : 0.f;
-  }
-  __syncthreads();
-
-  float rm[S::kSub], rw[S::kSub];
-#pragma unroll
-  for (int st = 0; st < S::kSub; ++st) {
-    rm[st] = -row_m[32 * st + col];
-    rw[st] = row_w[32 * st + col];
-  }
-
-  // ---- pass 2: softmax of every query, summed over the query block
-  float* srow = scores + (static_cast<size_t>(h) * NB + I) * NB;
-  for (int c = wave; c < n_chunks; c += kScoreWaves) {
-    f16x8 ahi[S::kKS], alo[S::kKS];
-    load_a(c, ahi, alo);
-    const bool tail = 32 * c + 32 > NB;
-    float colsum[16];
-#pragma unroll
-    for (int r = 0; r < 16; ++r) colsum[r] = 0.f;
-#pragma unroll
-    for (int st = 0; st < S::kSub; ++st) {
-      __builtin_amdgcn_sched_barrier(0);  // one sub-tile's registers live at a time
-      f32x16 acc = logits(ahi, alo, st);
-      if (tail) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * c + acc_row(r, hl) >= NB) acc[r] = -INFINITY;
-      }
-#pragma unroll
-      for (int r = 0; r < 16; ++r) colsum[r] += __builtin_amdgcn_exp2f(fmaf(acc[r], sc[st], rm[st])) * rw[st];
-    }
-    // Sum over the 32 query rows held by the 32 lanes of this half, as a
-    // reduce-scatter: at the exchange over lane bit b a lane keeps the half of
-    // its values that matches its bit and adds the partner's copy of them.
-    // Lane `col` ends with the total of accumulator register col >> 1.
-    const float total = reduce_scatter_32(colsum, col);
-    if ((col & 1) == 0) {
-      const int J = 32 * c + acc_row(col >> 1, hl);
-      if (J < NB) srow[J] = total;
-    }
-  }
+  finish(nc - 1);
 }
 
 template <typename T, int D>
@@ -378,11 +439,11 @@ hipError_t launch_scoring_t(const Problem& p, const void* q, const void* k,
   if (e != hipSuccess) return e;
   const int grid = p.heads * p.nb;
   if (p.block == 128)
-    hipLaunchKernelGGL((score_kernel<T, D, 128>), dim3(grid), dim3(kScoreThreads), 0, stream,
+    hipLaunchKernelGGL((score_kernel<T, D, 128, 4>), dim3(grid), dim3(256), 0, stream,
                        static_cast<const T*>(q), ws.khi, ws.klo, ws.inv_t, head_active, scores,
                        p.tokens, p.nb, NBp);
   else
-    hipLaunchKernelGGL((score_kernel<T, D, 64>), dim3(grid), dim3(kScoreThreads), 0, stream,
+    hipLaunchKernelGGL((score_kernel<T, D, 64, 4>), dim3(grid), dim3(128), 0, stream,
                        static_cast<const T*>(q), ws.khi, ws.klo, ws.inv_t, head_active, scores,
                        p.tokens, p.nb, NBp);
   return hipGetLastError();
