@@ -11,13 +11,13 @@
 //          [2^13, 2^14); Kbar*t_h = hi + lo with hi, lo fp16.  hi+lo holds
 //          22 significant bits, so the logits below are fp32-faithful.
 //   score: one workgroup per (head, query block).  Each query row is scaled
-//          by its own power of two and held as fp16 in LDS (exact for bf16
-//          input; fp32 input is split into two fp16 terms).  The logits
-//          S^T = Kbar Q^T run on the 32x32x16 fp16 matrix cores.  Pass 1
-//          forms each query's max and normaliser over all key blocks; pass 2
-//          recomputes the logits, forms the per-query softmax and sums it
-//          over the query block in a fixed order.  No atomics: the result is
-//          bitwise reproducible.
+//          by its own power of two and held as fp16 in registers (exact for
+//          bf16 input; fp32 input is split into two fp16 terms); the split
+//          pooled keys stream through an LDS ring.  The logits run on the
+//          32x32x16 fp16 matrix cores.  Pass 1 forms each query's max and
+//          normaliser over all key blocks; pass 2 recomputes the logits,
+//          forms the per-query softmax and sums it over the query block in a
+//          fixed order.  No atomics: the result is bitwise reproducible.
 #include <type_traits>
 
 #include "common.h"
