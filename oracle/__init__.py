@@ -21,6 +21,9 @@ that definition:
   abstract; HEART abstract), plus RAPID's Turbo re-selection on cached scores.
 * ``retrieval`` - block retrieval accuracy: each query block's dense attention
   mass per key block, and the mass a selection captures (PARK, Abstract).
+* ``correction`` - the cached correction of sparse attention by the attention
+  over its omitted blocks, weighted by the fresh sparse statistics (RECAP
+  abstract).
 
 What pins each function (closed forms, invariants, brute force, independent
 library routines) is in ``tests/test_oracle.py``; no function here is left
@@ -33,10 +36,12 @@ from .attention import block_sparse_attention, token_mask
 from .drift import drift, refresh_decision
 from .trajectory import cache_trajectory, turbo_schedule
 from .retrieval import captured_mass, dense_block_mass
+from .correction import complement_lists, corrected_trajectory, merge_partial, omitted_attention
 
 __all__ = [
     "block_bounds", "num_blocks", "pool_keys", "score_blocks", "score_head",
     "score_blocks_pooled_query", "select_row", "select_topp", "density",
     "block_sparse_attention", "token_mask", "drift", "refresh_decision",
     "cache_trajectory", "turbo_schedule", "dense_block_mass", "captured_mass",
+    "complement_lists", "omitted_attention", "merge_partial", "corrected_trajectory",
 ]

@@ -451,3 +451,120 @@ def test_captured_mass():
     assert O.captured_mass(m, [[0], [2], []]) == pytest.approx((0.5 + 0.7 + 0.0) / 3, abs=1e-15)
     assert O.captured_mass(m, [[0, 1, 2]] * 3) == pytest.approx(1.0, abs=1e-15)
     assert O.captured_mass(m, [[1, 2], [0, 1], [2]]) == pytest.approx((0.5 + 0.3 + 1 / 3) / 3, abs=1e-15)
+
+
+# ------------------------------------------------------- cached correction
+
+def _random_lists(rng, nb, rows, extra=()):
+    """Block lists read as sets: random order, repeats and out-of-range entries."""
+    out = []
+    for r in range(rows):
+        c = int(rng.integers(0, nb + 1))
+        lst = list(rng.choice(nb, c, replace=False)) + list(extra)
+        if c and rng.random() < 0.5:
+            lst.append(lst[0])                       # a repeat
+        if rng.random() < 0.3:
+            lst.append(nb + 3)                       # ignored
+        rng.shuffle(lst)
+        out.append(np.array(lst, np.int64))
+    return out
+
+
+def test_complement_lists_brute_force():
+    rng = np.random.default_rng(71)
+    for nb in (1, 2, 5, 9):
+        for row, comp in zip(*(lambda l: (l, O.complement_lists(l, nb)))(_random_lists(rng, nb, 30))):
+            listed = {int(j) for j in row if 0 <= j < nb}
+            assert list(comp) == [j for j in range(nb) if j not in listed]
+    assert [list(c) for c in O.complement_lists([[], [0, 1, 2]], 3)] == [[0, 1, 2], []]
+
+
+@pytest.mark.parametrize("n,b,d", [(40, 8, 4), (37, 8, 5), (64, 16, 8)])
+def test_sparse_merged_with_omitted_is_dense(n, b, d):
+    """Attention over a list and over its complement join to dense attention,
+    whatever the list (empty, full or partial, ragged last block)."""
+    rng = np.random.default_rng(n * d)
+    q, k, v = (_rand((n, d), 80 + i, 0.7) for i in range(3))
+    nb = O.num_blocks(n, b)
+    lists = _random_lists(rng, nb, nb)
+    lists[0] = np.array([], np.int64)
+    lists[-1] = np.arange(nb)
+    o_s, l_s = O.block_sparse_attention(q, k, v, b, lists)
+    o_o, l_o = O.omitted_attention(q, k, v, b, lists)
+    out, lse = O.merge_partial(o_s, l_s, o_o, l_o)
+    np.testing.assert_allclose(out, _sdpa(q, k, v), atol=1e-13)
+    logits = torch.from_numpy(q @ k.T / np.sqrt(d))
+    np.testing.assert_allclose(lse, torch.logsumexp(logits, dim=1).numpy(), atol=1e-13)
+    # the two parts really are disjoint: full list -> nothing omitted
+    assert np.isneginf(l_o[(nb - 1) * b:]).all() and (o_o[(nb - 1) * b:] == 0).all()
+
+
+def test_merge_with_an_empty_part():
+    o = _rand((6, 3), 90)
+    l = _rand(6, 91)
+    z, ninf = np.zeros((6, 3)), np.full(6, -np.inf)
+    out, lse = O.merge_partial(o, l, z, ninf)
+    assert (out == o).all() and (lse == l).all()
+    out, lse = O.merge_partial(z, ninf, o, l)
+    assert (out == o).all() and (lse == l).all()
+    out, lse = O.merge_partial(z, ninf, z, ninf)
+    assert (out == 0).all() and np.isneginf(lse).all()
+
+
+def test_merge_weights_closed_form():
+    """Equal log-sum-exps average the parts; a gap of log 3 weights them 3:1."""
+    a, b_ = np.array([[1.0, -2.0]]), np.array([[5.0, 2.0]])
+    out, lse = O.merge_partial(a, np.array([0.4]), b_, np.array([0.4]))
+    np.testing.assert_allclose(out, [[3.0, 0.0]], atol=1e-15)
+    np.testing.assert_allclose(lse, [0.4 + np.log(2.0)], atol=1e-15)
+    out, lse = O.merge_partial(a, np.array([np.log(3.0)]), b_, np.array([0.0]))
+    np.testing.assert_allclose(out, [[2.0, -1.0]], atol=1e-15)
+    np.testing.assert_allclose(lse, [np.log(4.0)], atol=1e-15)
+
+
+def test_stale_omitted_part_is_exact_when_only_listed_blocks_change():
+    """Keys and values of blocks every row keeps change; the omitted blocks do
+    not.  The cached omitted part then still holds exactly, and the merge with
+    the fresh sparse pass is dense attention on the new inputs."""
+    n, b, d = 45, 8, 6
+    nb = O.num_blocks(n, b)
+    rng = np.random.default_rng(5)
+    q = _rand((n, d), 100, 0.6)
+    k0, v0 = _rand((n, d), 101, 0.6), _rand((n, d), 102)
+    lists = _random_lists(rng, nb, nb, extra=(0, nb - 1))    # every row keeps 0 and the ragged last block
+    k1, v1 = k0.copy(), v0.copy()
+    for j in (0, nb - 1):
+        lo, hi = O.block_bounds(j, n, b)
+        k1[lo:hi] += _rand((hi - lo, d), 103 + j, 0.5)
+        v1[lo:hi] = _rand((hi - lo, d), 105 + j)
+    cached = O.omitted_attention(q, k0, v0, b, lists)
+    out, _ = O.merge_partial(*O.block_sparse_attention(q, k1, v1, b, lists), *cached)
+    np.testing.assert_allclose(out, _sdpa(q, k1, v1), atol=1e-13)
+
+
+def test_corrected_trajectory_refresh_is_dense_and_v_change_is_closed_form():
+    """Step 0 (every head refreshed) is dense attention.  Step 1 changes only
+    V, so no head refreshes: the output is dense attention with the new values
+    on the kept blocks and the refresh step's values on the omitted ones."""
+    h, n, b, d = 2, 40, 8, 4
+    q, k = _rand((h, n, d), 110, 0.8), _rand((h, n, d), 111, 0.8)
+    v0, v1 = _rand((h, n, d), 112), _rand((h, n, d), 113)
+    steps = list(O.corrected_trajectory([(q, k, v0), (q, k, v1)], b, [0.6, 0.8], tau=0.05))
+    refresh, lists, out, lse, s_out, _ = steps[0]
+    assert refresh.all()
+    for a in range(h):
+        np.testing.assert_allclose(out[a], _sdpa(q[a], k[a], v0[a]), atol=1e-13)
+        logits = torch.from_numpy(q[a] @ k[a].T / np.sqrt(d))
+        np.testing.assert_allclose(lse[a], torch.logsumexp(logits, dim=1).numpy(), atol=1e-13)
+    assert np.abs(s_out - out).max() > 1e-3          # the correction is not a no-op here
+    refresh, lists1, out, _, _, _ = steps[1]
+    assert not refresh.any() and all(
+        (np.asarray(x) == np.asarray(y)).all() for la, lb in zip(lists, lists1) for x, y in zip(la, lb))
+    nb = O.num_blocks(n, b)
+    for a in range(h):
+        for i in range(nb):
+            lo, hi = O.block_bounds(i, n, b)
+            kept = O.token_mask(n, b, lists[a][i])
+            vmix = np.where(kept[:, None], v1[a], v0[a])
+            want = _sdpa(q[a, lo:hi], k[a], vmix)
+            np.testing.assert_allclose(out[a, lo:hi], want, atol=1e-13)
