@@ -3,18 +3,21 @@
 The hot path is four library calls (include/rsa.h): PARK block scoring,
 top-p selection, the per-head drift check of Temporal Mask Reuse and
 block-sparse flash attention.  Two more calls measure block retrieval
-accuracy (dense block mass, query-pooled comparison scores).  This package is
-only their ctypes binding plus the host loop that reuses cached masks across
-denoising steps.
+accuracy (dense block mass, query-pooled comparison scores) and two carry
+RECAP's cached correction (attention over the omitted blocks, and the join of
+two attentions over disjoint key sets).  This package is only their ctypes
+binding plus the host loop that reuses cached masks across denoising steps.
 """
-from .binding import (Problem, RsaError, RsaLibraryMissing, block_sparse_attn, declared_functions,
+from .binding import (Problem, RsaError, RsaLibraryMissing, attn_merge, attn_omitted,
+                      block_sparse_attn, declared_functions,
                       dense_block_mass, lib, make_problem, mask_drift, score_blocks,
                       score_blocks_pooled, select_topp, workspace_bytes, OP_ATTN, OP_DRIFT,
                       OP_POOLED, OP_SCORE, OP_SELECT, RSA_BF16, RSA_FP32, LIB_PATH)
 from .cache import MaskCache
 
 __all__ = [
-    "Problem", "RsaError", "RsaLibraryMissing", "block_sparse_attn", "declared_functions",
+    "Problem", "RsaError", "RsaLibraryMissing", "attn_merge", "attn_omitted", "block_sparse_attn",
+    "declared_functions",
     "dense_block_mass", "lib", "make_problem", "mask_drift", "score_blocks", "score_blocks_pooled",
     "select_topp", "workspace_bytes", "MaskCache", "OP_ATTN", "OP_DRIFT", "OP_POOLED", "OP_SCORE",
     "OP_SELECT", "RSA_BF16", "RSA_FP32", "LIB_PATH",

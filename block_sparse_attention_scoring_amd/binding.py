@@ -73,6 +73,8 @@ def _declare(lib):
         "rsa_block_sparse_attn": (i32, [pp, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
         "rsa_dense_block_mass": (i32, [pp, _P, _P, _P, _P]),
         "rsa_score_blocks_pooled": (i32, [pp, _P, _P, _P, _P, sz, _P]),
+        "rsa_attn_omitted": (i32, [pp, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
+        "rsa_attn_merge": (i32, [pp, _P, _P, _P, _P, _P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -216,3 +218,27 @@ def score_blocks_pooled(q, k, p: Problem, out=None, workspace=None):
     _check(lib().rsa_score_blocks_pooled(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(out), _ptr(ws), wsb,
                                          _stream(q)), "rsa_score_blocks_pooled")
     return out
+
+
+def attn_omitted(q, k, v, counts, block_idx, p: Problem, head_active=None, out=None, lse=None,
+                 workspace=None):
+    """Attention over the key blocks each row's list leaves out -> (out like q, lse fp32 [H, N]).
+
+    Heads with head_active[h] == 0 keep what ``out``/``lse`` held (pass the
+    cache's buffers to refresh only some heads)."""
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((p.heads, p.tokens), dtype=torch.float32, device=q.device)
+    ws, wsb = _workspace(p, OP_ATTN, q.device, workspace)
+    _check(lib().rsa_attn_omitted(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(counts),
+                                  _ptr(block_idx), _ptr(head_active), _ptr(out), _ptr(lse), _ptr(ws),
+                                  wsb, _stream(q)), "rsa_attn_omitted")
+    return out, lse
+
+
+def attn_merge(out, lse, part_out, part_lse, p: Problem):
+    """In place: (out, lse) <- attention over the union of two disjoint key sets."""
+    _check(lib().rsa_attn_merge(ctypes.byref(p), _ptr(out), _ptr(lse), _ptr(part_out), _ptr(part_lse),
+                                _stream(out)), "rsa_attn_merge")
+    return out, lse

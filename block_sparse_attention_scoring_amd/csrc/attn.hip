@@ -50,14 +50,18 @@ constexpr int kMaxNB = 4096;  // largest number of blocks per sequence
 // Canonical lists.  One workgroup per (query block I, head h): marks the
 // listed blocks in an LDS byte map and compacts the map in ascending order
 // into clist[h, I, 0..ccount[h, I]).  The count is clamped to [0, NB] and
-// indices outside [0, NB) are dropped.
+// indices outside [0, NB) are dropped.  With `complement` set, the blocks
+// the row does not list are compacted instead.  Heads with head_active[h]
+// == 0 are skipped (head_active NULL: every head).
 __global__ __launch_bounds__(256) void canon_kernel(const int* __restrict__ counts,
                                                     const int* __restrict__ block_idx,
-                                                    int* __restrict__ ccount, int* __restrict__ clist,
-                                                    int NB) {
+                                                    const uint8_t* __restrict__ head_active,
+                                                    int complement, int* __restrict__ ccount,
+                                                    int* __restrict__ clist, int NB) {
   __shared__ uint8_t mark[kMaxNB];
   __shared__ int wsum[4];
   const int I = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  if (head_active != nullptr && head_active[h] == 0) return;
   const int lane = tid & 63, wave = tid >> 6;
   const size_t row = static_cast<size_t>(h) * NB + I;
   for (int e = tid; e < NB; e += 256) mark[e] = 0;
@@ -72,7 +76,7 @@ __global__ __launch_bounds__(256) void canon_kernel(const int* __restrict__ coun
   int base = 0;
   for (int r0 = 0; r0 < NB; r0 += 256) {
     const int e = r0 + tid;
-    const bool f = e < NB && mark[e] != 0;
+    const bool f = e < NB && (mark[e] != 0) != (complement != 0);
     const uint64_t bal = __ballot(f);
     const int pre = __builtin_popcountll(bal & ((1ull << lane) - 1));
     if (lane == 0) wsum[wave] = __builtin_popcountll(bal);
@@ -112,9 +116,11 @@ struct AttnShape {
 // zeros past the last token: the operand layout of O^T = V^T P^T.
 template <int D, int B>
 __global__ __launch_bounds__(256) void vt_kernel(const uint16_t* __restrict__ v,
+                                                 const uint8_t* __restrict__ head_active,
                                                  uint16_t* __restrict__ vt, int N, int NB) {
   __shared__ uint16_t tile[B][D + 2];
   const int J = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  if (head_active != nullptr && head_active[h] == 0) return;
   const int kbase = J * B, bJ = min(B, N - kbase);
   const size_t np = static_cast<size_t>(NB) * B;
   for (int c = tid; c < B * D / 8; c += 256) {
@@ -154,8 +160,8 @@ template <int D, int B, int KS, int NBUF>
 __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const int* __restrict__ ccount,
-    const int* __restrict__ clist, uint16_t* __restrict__ out,
-    float* __restrict__ lse, int H, int N, int NB, float scale_log2) {
+    const int* __restrict__ clist, const uint8_t* __restrict__ head_active,
+    uint16_t* __restrict__ out, float* __restrict__ lse, int H, int N, int NB, float scale_log2) {
   using S = AttnShape<D, B, KS, NBUF>;
   static_assert(NBUF >= 3 && NBUF <= 4, "ring of 3 or 4 LDS slots");
   // Ring slots: K sub-tile at [0, kTile), V^T sub-tile after it.  Separate
@@ -174,6 +180,7 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int h = slot / per_xcd, I = xcd * per_xcd + slot % per_xcd;
   if (h >= H || I >= NB) return;
+  if (head_active != nullptr && head_active[h] == 0) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS addresses stay scalar
@@ -415,12 +422,14 @@ template <int D, int B>
 __global__ __launch_bounds__(B) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int* __restrict__ ccount, const int* __restrict__ clist,
-    float* __restrict__ out, float* __restrict__ lse, int N, int NB, float scale_log2) {
+    const uint8_t* __restrict__ head_active, float* __restrict__ out, float* __restrict__ lse,
+    int N, int NB, float scale_log2) {
   constexpr int kChunk = 32;
   __shared__ float Ks[kChunk * D];
   __shared__ float Vs[kChunk * D];
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int h = tile / NB, I = tile - h * NB;
+  if (head_active != nullptr && head_active[h] == 0) return;
   const int tid = threadIdx.x;
   const int qrow = I * B + tid;
   const size_t head_off = static_cast<size_t>(h) * N * D;
@@ -499,14 +508,15 @@ AttnWs attn_ws_layout(const Problem& p) {
 
 template <int D, int B>
 hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const void* v,
-                         const int* counts, const int* idx, void* out, float* lse, void* ws,
-                         hipStream_t stream) {
+                         const int* counts, const int* idx, const uint8_t* head_active,
+                         int complement, void* out, float* lse, void* ws, hipStream_t stream) {
   const float sl2 = p.scale * kLog2e;
   const AttnWs w = attn_ws_layout(p);
   char* base = static_cast<char*>(ws);
   int* ccount = reinterpret_cast<int*>(base + w.ccount_off);
   int* clist = reinterpret_cast<int*>(base + w.clist_off);
-  hipLaunchKernelGGL(canon_kernel, dim3(p.nb, p.heads), dim3(256), 0, stream, counts, idx, ccount, clist, p.nb);
+  hipLaunchKernelGGL(canon_kernel, dim3(p.nb, p.heads), dim3(256), 0, stream, counts, idx, head_active,
+                     complement, ccount, clist, p.nb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.dtype == 0) {
@@ -516,18 +526,18 @@ hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const v
     using S = AttnShape<D, B, kKs, kNbuf>;
     uint16_t* vt = reinterpret_cast<uint16_t*>(base);
     hipLaunchKernelGGL((vt_kernel<D, B>), dim3(p.nb, p.heads), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(v), vt, p.tokens, p.nb);
+                       static_cast<const uint16_t*>(v), head_active, vt, p.tokens, p.nb);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int grid = 8 * ((p.nb + 7) / 8) * p.heads;
     hipLaunchKernelGGL((attn_bf16_kernel<D, B, kKs, kNbuf>), dim3(grid), dim3(S::kThreads), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt, ccount,
-                       clist, static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2);
+                       clist, head_active, static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2);
   } else {
     hipLaunchKernelGGL((attn_f32_kernel<D, B>), dim3(p.heads * p.nb), dim3(B), 0, stream,
                        static_cast<const float*>(q), static_cast<const float*>(k),
-                       static_cast<const float*>(v), ccount, clist, static_cast<float*>(out),
-                       lse, p.tokens, p.nb, sl2);
+                       static_cast<const float*>(v), ccount, clist, head_active,
+                       static_cast<float*>(out), lse, p.tokens, p.nb, sl2);
   }
   return hipGetLastError();
 }
@@ -537,12 +547,13 @@ hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const v
 size_t attn_ws_bytes(const Problem& p) { return attn_ws_layout(p).total; }
 
 hipError_t launch_attention(const Problem& p, const void* q, const void* k, const void* v,
-                            const int* counts, const int* idx, void* out, float* lse, void* ws,
-                            hipStream_t stream) {
-  if (p.head_dim == 128 && p.block == 128) return launch_attn_t<128, 128>(p, q, k, v, counts, idx, out, lse, ws, stream);
-  if (p.head_dim == 128 && p.block == 64) return launch_attn_t<128, 64>(p, q, k, v, counts, idx, out, lse, ws, stream);
-  if (p.head_dim == 64 && p.block == 128) return launch_attn_t<64, 128>(p, q, k, v, counts, idx, out, lse, ws, stream);
-  return launch_attn_t<64, 64>(p, q, k, v, counts, idx, out, lse, ws, stream);
+                            const int* counts, const int* idx, const uint8_t* head_active,
+                            int complement, void* out, float* lse, void* ws, hipStream_t stream) {
+  auto go = [&](auto fn) { return fn(p, q, k, v, counts, idx, head_active, complement, out, lse, ws, stream); };
+  if (p.head_dim == 128 && p.block == 128) return go(launch_attn_t<128, 128>);
+  if (p.head_dim == 128 && p.block == 64) return go(launch_attn_t<128, 64>);
+  if (p.head_dim == 64 && p.block == 128) return go(launch_attn_t<64, 128>);
+  return go(launch_attn_t<64, 64>);
 }
 
 }  // namespace rsa

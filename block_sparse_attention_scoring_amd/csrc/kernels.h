@@ -39,11 +39,18 @@ hipError_t launch_select(const Problem& p, const float* scores, const float* top
 hipError_t launch_drift(const Problem& p, const void* q, const void* k, void* q_ref,
                         void* k_ref, float threshold, int update_ref, float* drift,
                         uint8_t* refresh, void* ws, hipStream_t stream);
-// bf16 attention workspace: V transposed to [H, D, NB*B] (0 for fp32).
+// Attention workspace: (bf16) V re-laid out for the matrix cores, then the
+// canonical counts and lists.  With `complement` set the attention runs over
+// the blocks each row does not list; heads with head_active[h] == 0 (when
+// head_active is not NULL) are skipped and their outputs left untouched.
 size_t attn_ws_bytes(const Problem& p);
 hipError_t launch_attention(const Problem& p, const void* q, const void* k, const void* v,
-                            const int* counts, const int* idx, void* out, float* lse, void* ws,
-                            hipStream_t stream);
+                            const int* counts, const int* idx, const uint8_t* head_active,
+                            int complement, void* out, float* lse, void* ws, hipStream_t stream);
+// In place: (out, lse) <- attention over the union of the key sets behind
+// (out, lse) and (part, part_lse), two disjoint parts.
+hipError_t launch_merge(const Problem& p, void* out, float* lse, const void* part,
+                        const float* part_lse, hipStream_t stream);
 
 // Block means of x [H, N, D] times `mul`, written as fp32 [H, NB, D] (the
 // scoring pool kernel; bmax gets each block's max |.|).

@@ -29,6 +29,12 @@
  * attention mass per key block, and rsa_score_blocks_pooled the comparison
  * scorer that averages the queries before the softmax.
  *
+ * Two calls carry the cached correction of RECAP (Reciprocal Sparse Attention
+ * and Hierarchical Caching for Efficient Video Diffusion, Abstract):
+ * rsa_attn_omitted computes, at a mask refresh, the attention over the key
+ * blocks each list leaves out, to be cached; rsa_attn_merge joins a fresh
+ * sparse output with that cached part, weighted by their log-sum-exps.
+ *
  * Common conventions
  * ------------------
  * Tensors q, k, v, out are [heads, tokens, head_dim], row-major, tokens in
@@ -257,6 +263,52 @@ rsa_status rsa_dense_block_mass(const rsa_problem* p, const void* q, const void*
  */
 rsa_status rsa_score_blocks_pooled(const rsa_problem* p, const void* q, const void* k,
                                    float* pooled, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Attention over the omitted key blocks (RECAP, Abstract: a dense refinement,
+ * computed at refresh time and cached, for the interactions that sparse
+ * attention leaves out).  For query i of block I of head h, the visible keys
+ * are the tokens of every key block that row (h, I) does NOT list:
+ *
+ *   out[h,i,:] = sum_{t omitted} softmax_t(scale * <q_i, k_t>) v_t,
+ *   lse[h,i]   = log sum_{t omitted} exp(scale * <q_i, k_t>).
+ *
+ * A row that lists every block has nothing omitted: out = 0, lse = -inf.
+ * Lists are read as in rsa_block_sparse_attn (any order, repeats once,
+ * counts clamped to [0, NB], invalid entries ignored).  Joined with the
+ * sparse pass over the same list by rsa_attn_merge it gives dense attention.
+ * head_active: [heads] u8 or NULL (all heads).  Heads with head_active[h] == 0
+ * are skipped: their rows of out and lse keep what they held, so the outputs
+ * can be a per-head cache refreshed with rsa_mask_drift's refresh flags.
+ * q, k, v, out: as in rsa_block_sparse_attn; lse: [heads, tokens] fp32
+ * output (required).  ws / ws_bytes: at least rsa_workspace_bytes(p,
+ * RSA_OP_ATTN), laid out as for rsa_block_sparse_attn (the canonical lists
+ * hold the omitted blocks).
+ * Non-finite values in q, k or v give undefined results.
+ */
+rsa_status rsa_attn_omitted(const rsa_problem* p, const void* q, const void* k, const void* v,
+                            const int32_t* counts, const int32_t* block_idx,
+                            const uint8_t* head_active, void* out, float* lse, void* ws,
+                            size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Join two attentions over disjoint key sets, in place (RECAP, Abstract: the
+ * cached refinement corrects each fresh sparse output, and the fresh sparse
+ * statistics set how much the ageing cached part counts).  Per row r of the
+ * heads * tokens rows, with L = log(exp(lse[r]) + exp(part_lse[r])):
+ *
+ *   out[r,:] <- exp(lse[r] - L) out[r,:] + exp(part_lse[r] - L) part_out[r,:],
+ *   lse[r]   <- L.
+ *
+ * A part with lse = -inf has weight 0; both -inf give out = 0, lse = -inf.
+ * out, part_out: [heads, tokens, head_dim] of `dtype`, 16-byte aligned (bf16
+ * results rounded to nearest even; fp32 arithmetic).  lse, part_lse:
+ * [heads, tokens] fp32.  No workspace.  Typical use: out/lse from
+ * rsa_block_sparse_attn on the current step, part_out/part_lse the cache
+ * rsa_attn_omitted wrote when the head's mask was last refreshed.
+ */
+rsa_status rsa_attn_merge(const rsa_problem* p, void* out, float* lse, const void* part_out,
+                          const float* part_lse, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -42,7 +42,8 @@ def test_exports_every_declared_symbol(lib):
     names = R.declared_functions()
     assert set(names) == {"rsa_workspace_bytes", "rsa_status_str", "rsa_version", "rsa_score_blocks",
                           "rsa_select_topp", "rsa_mask_drift", "rsa_block_sparse_attn",
-                          "rsa_dense_block_mass", "rsa_score_blocks_pooled"}
+                          "rsa_dense_block_mass", "rsa_score_blocks_pooled", "rsa_attn_omitted",
+                          "rsa_attn_merge"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -112,6 +113,11 @@ def test_null_problem_and_pointers(lib):
     assert lib.rsa_dense_block_mass(ctypes.byref(p), b.ptr, b.ptr, None, None) == NULL
     assert lib.rsa_dense_block_mass(None, b.ptr, b.ptr, b.ptr, None) == NULL
     assert lib.rsa_score_blocks_pooled(ctypes.byref(p), b.ptr, None, b.ptr, b.ptr, 1 << 30, None) == NULL
+    # the omitted-block attention needs its lse (the cache's weight)
+    assert lib.rsa_attn_omitted(ctypes.byref(p), b.ptr, b.ptr, b.ptr, b.ptr, b.ptr, None, b.ptr, None,
+                                b.ptr, 1 << 30, None) == NULL
+    assert lib.rsa_attn_merge(ctypes.byref(p), b.ptr, b.ptr, b.ptr, None, None) == NULL
+    assert lib.rsa_attn_merge(None, b.ptr, b.ptr, b.ptr, b.ptr, None) == NULL
     assert b.untouched()
 
 
@@ -124,6 +130,9 @@ def test_alignment(lib):
     assert lib.rsa_score_blocks(ctypes.byref(p), b.ptr, b.ptr, None, mis, b.ptr, 1 << 30, None) == ALIGN
     assert lib.rsa_dense_block_mass(ctypes.byref(p), b.ptr, mis, b.ptr, None) == ALIGN
     assert lib.rsa_score_blocks_pooled(ctypes.byref(p), b.ptr, b.ptr, mis, b.ptr, 1 << 30, None) == ALIGN
+    assert lib.rsa_attn_omitted(ctypes.byref(p), b.ptr, b.ptr, b.ptr, b.ptr, b.ptr, None, mis, b.ptr,
+                                b.ptr, 1 << 30, None) == ALIGN
+    assert lib.rsa_attn_merge(ctypes.byref(p), b.ptr, b.ptr, mis, b.ptr, None) == ALIGN
     assert b.untouched()
 
 
@@ -138,6 +147,8 @@ def test_workspace_checks(lib):
     aneed = B.workspace_bytes(p, B.OP_ATTN)
     assert lib.rsa_block_sparse_attn(ctypes.byref(p), b.ptr, b.ptr, b.ptr, b.ptr, b.ptr, b.ptr, None,
                                      b.ptr, aneed - 1, None) == WS
+    assert lib.rsa_attn_omitted(ctypes.byref(p), b.ptr, b.ptr, b.ptr, b.ptr, b.ptr, None, b.ptr, b.ptr,
+                                b.ptr, aneed - 1, None) == WS
     pneed = B.workspace_bytes(p, B.OP_POOLED)
     assert lib.rsa_score_blocks_pooled(ctypes.byref(p), b.ptr, b.ptr, b.ptr, b.ptr, pneed - 1, None) == WS
     assert lib.rsa_score_blocks_pooled(ctypes.byref(p), b.ptr, b.ptr, b.ptr, None, pneed, None) == WS

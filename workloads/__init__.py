@@ -25,7 +25,9 @@ Recipe (per config ``c``, head ``h``):
 Seeds come from ``numpy.random.SeedSequence([c, h, tensor_id, step])`` with
 ``tensor_id`` q=0, k=1, v=2, field parameters 10/11, head sharpness 20.
 The trajectory config perturbs the fp32 masters of q and k once per step by
-``0.02 * N(0, 1)`` (a random walk) and casts every step to bf16.
+``0.02 * N(0, 1)`` (a random walk) and casts every step to bf16; with
+``values=True`` the v master takes the same walk (for the cached correction,
+whose omitted part ages as the values move).
 """
 from __future__ import annotations
 
@@ -164,6 +166,7 @@ class Inputs:
     top_p: np.ndarray        # [H] float32
     q_master: np.ndarray | None = None   # fp32 masters, kept for trajectories
     k_master: np.ndarray | None = None
+    v_master: np.ndarray | None = None
 
 
 def make_inputs(wl: Workload, alpha: float = ALPHA, heads: Sequence[int] | None = None,
@@ -183,12 +186,14 @@ def make_inputs(wl: Workload, alpha: float = ALPHA, heads: Sequence[int] | None 
     p = wl.top_p_array()[hs]
     out = Inputs(wl, _cast(qm, wl.dtype), _cast(km, wl.dtype), _cast(vm, wl.dtype), p)
     if keep_masters:
-        out.q_master, out.k_master = qm, km
+        out.q_master, out.k_master, out.v_master = qm, km, vm
     return out
 
 
-def drift_step(inp: Inputs, step: int, heads: Sequence[int] | None = None) -> None:
-    """Advance the q/k fp32 masters by one random-walk step and re-cast."""
+def drift_step(inp: Inputs, step: int, heads: Sequence[int] | None = None,
+               values: bool = False) -> None:
+    """Advance the q/k (and with ``values``, v) fp32 masters by one random-walk
+    step and re-cast."""
     wl = inp.workload
     assert inp.q_master is not None, "make_inputs(..., keep_masters=True) first"
     hs = list(range(wl.heads)) if heads is None else list(heads)
@@ -199,11 +204,15 @@ def drift_step(inp: Inputs, step: int, heads: Sequence[int] | None = None) -> No
         h = hs[i]
         inp.q_master[i] += s * noise(wl.cid, h, TID_Q, step, n, d)
         inp.k_master[i] += s * noise(wl.cid, h, TID_K, step, n, d)
+        if values:
+            inp.v_master[i] += s * noise(wl.cid, h, TID_V, step, n, d)
 
     with ThreadPoolExecutor(_threads()) as ex:
         list(ex.map(one, range(len(hs))))
     inp.q = _cast(inp.q_master, wl.dtype)
     inp.k = _cast(inp.k_master, wl.dtype)
+    if values:
+        inp.v = _cast(inp.v_master, wl.dtype)
 
 
 def to_f64(t: torch.Tensor) -> np.ndarray:
