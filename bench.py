@@ -47,6 +47,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--retrieval", action="store_true",
                     help="report block retrieval accuracy (dense mass captured at equal density) instead")
+    ap.add_argument("--correction", action="store_true",
+                    help="report the cached correction over a drifting trajectory instead")
+    ap.add_argument("--traj-steps", type=int, default=8, help="trajectory length for --correction")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -233,18 +236,118 @@ def retrieval(args):
     print(json.dumps(res), flush=True)
 
 
+def correction(args):
+    """The cached correction over a drifting trajectory (RECAP, Abstract).
+
+    The 720p reuse workload's q, k and v take the generator's random walk for
+    ``--traj-steps`` steps while the mask cache runs with the correction on
+    (drift-gated mask refresh per head; the omitted-block attention of a head
+    is recomputed when its mask is).  Each step's corrected output and the
+    plain sparse output on the same cached lists are compared with dense
+    attention (the attention call given every block), as relative L2 errors.
+    Then, on the last step's inputs, the omitted-block pass over every head,
+    the sparse pass and the merge are timed with HIP events on the library's
+    stream; the merge, a streaming kernel, is priced against HBM bandwidth.
+    """
+    import numpy as np
+    import torch
+    import workloads as W
+    import block_sparse_attention_scoring_amd as R
+
+    wl = W.CONFIGS["reuse_720p"]
+    inp = W.make_inputs(wl, keep_masters=True)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    q = inp.q.to(dev)
+    p = R.make_problem(q, wl.grid, wl.block)
+    nb = wl.nblocks
+    cache = R.MaskCache(p, torch.from_numpy(inp.top_p).to(dev), wl.drift_threshold, correction=True)
+    full_c = torch.full((wl.heads, nb), nb, dtype=torch.int32, device=dev)
+    full_i = torch.arange(nb, dtype=torch.int32, device=dev).repeat(wl.heads, nb, 1).contiguous()
+
+    def rel(a, b):
+        d = (a.float() - b.float()).flatten(1).norm(dim=1)
+        return (d / b.float().flatten(1).norm(dim=1)).cpu().numpy()
+
+    per_step = []
+    refresh_total = np.zeros(wl.heads, int)
+    for s in range(args.traj_steps):
+        if s > 0:
+            W.drift_step(inp, s, values=True)
+        q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+        out, _ = cache.step(q, k, v)
+        sparse, _ = R.block_sparse_attn(q, k, v, cache.counts, cache.block_idx, p, want_lse=False)
+        dense, _ = R.block_sparse_attn(q, k, v, full_c, full_i, p, want_lse=False)
+        e_c, e_s = rel(out, dense), rel(sparse, dense)
+        fl = cache.refresh.cpu().numpy() if s > 0 else np.ones(wl.heads, np.uint8)
+        refresh_total += fl
+        per_step.append({"step": s, "refreshed_heads": int(fl.sum()),
+                         "density": round(float(cache.density.mean().item()), 4),
+                         "rel_err_sparse": round(float(e_s.mean()), 5),
+                         "rel_err_corrected": round(float(e_c.mean()), 5),
+                         "rel_err_corrected_max_head": round(float(e_c.max()), 5)})
+        print(json.dumps({"progress": per_step[-1]}), file=sys.stderr, flush=True)
+        del out, sparse, dense
+
+    def timed(fn, reps=5):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ws = cache.attn_ws
+    o_out, o_lse = torch.empty_like(q), torch.empty((wl.heads, wl.tokens), dtype=torch.float32, device=dev)
+    s_out, s_lse = torch.empty_like(q), torch.empty_like(o_lse)
+    t_omit = timed(lambda: R.attn_omitted(q, k, v, cache.counts, cache.block_idx, p, out=o_out, lse=o_lse,
+                                          workspace=ws))
+    t_sparse = timed(lambda: R.block_sparse_attn(q, k, v, cache.counts, cache.block_idx, p, out=s_out,
+                                                 lse=s_lse, workspace=ws))
+    m_out, m_lse = s_out.clone(), s_lse.clone()
+    t_merge = timed(lambda: R.attn_merge(m_out, m_lse, o_out, o_lse, p), reps=20)
+    rows = wl.heads * wl.tokens
+    merge_bytes = rows * (3 * wl.head_dim * 2 + 3 * 4)
+    dens = float(cache.density.mean().item())
+    res = {
+        "mode": "correction",
+        "metric": "relative L2 error against dense attention, mean over heads (lower is better)",
+        "workload": wl.name, "heads": wl.heads, "tokens": wl.tokens, "block": wl.block,
+        "top_p": float(inp.top_p[0]), "drift_threshold": wl.drift_threshold,
+        "data": "synthetic (seeded smooth 3-D field + noise; q, k, v random walk per step; no weights)",
+        "steps": per_step,
+        "refreshes_per_head": {"min": int(refresh_total.min()), "max": int(refresh_total.max()),
+                               "mean": round(float(refresh_total.mean()), 2)},
+        "ms": {"omitted_all_heads": round(t_omit, 3), "sparse": round(t_sparse, 3),
+               "merge": round(t_merge, 4)},
+        "final_density": round(dens, 4),
+        "merge_roofline": {"bound": "hbm", "bytes": merge_bytes,
+                           "achieved": round(merge_bytes / (t_merge * 1e-3) / 1e9, 1),
+                           "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                           "frac": round(merge_bytes / (t_merge * 1e-3) / 1e9 / PEAK_HBM_GBS, 3)},
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py runs on exactly one GPU: the four kernels work per head with no "
-              "exchange between GPUs, so a multi-GPU run is not provided (see DESIGN.md "
-              "for how heads would shard).", file=sys.stderr)
+              "exchange between GPUs, so a multi-GPU run is not provided; sharding the heads "
+              "over GPUs would run this same path on each GPU's share of heads.", file=sys.stderr)
         sys.exit(2)
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
     if args.retrieval:
         retrieval(args)
+        return
+    if args.correction:
+        correction(args)
         return
 
     import numpy as np
