@@ -249,6 +249,23 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
   float m_run = -INFINITY;  // reference maximum, log2 units
   float l_part[4] = {0.f, 0.f, 0.f, 0.f};
 
+  // Per-lane byte offsets of the operand reads inside a slot, one per
+  // k-step: the swizzle repeats every 16 rows, so rows 32t + col share col's
+  // swizzle and a read is slot + 32-row block + this offset.
+  // The empty asm keeps each offset whole, so the constant part of an
+  // address goes into the LDS read's immediate offset instead of a vector add.
+  uint32_t klane[S::kKSD], vlane[S::kKSK];
+#pragma unroll
+  for (int s = 0; s < S::kKSD; ++s) {
+    klane[s] = static_cast<uint32_t>(col * (2 * D) + (((2 * s + hl) ^ swz<S::kCprK>(col)) * 16));
+    asm volatile("" : "+v"(klane[s]));
+  }
+#pragma unroll
+  for (int w = 0; w < S::kKSK; ++w) {
+    vlane[w] = static_cast<uint32_t>(col * (2 * KS) + (((2 * w + hl) ^ swz<S::kCprV>(col)) * 16));
+    asm volatile("" : "+v"(vlane[w]));
+  }
+
   // S^T of one sub-tile (keys x this wave's queries) from the K slot `cur`
   auto qk = [&](const uint16_t* cur, f32x16* sacc) {
     const char* kt = reinterpret_cast<const char*>(cur);
@@ -258,10 +275,8 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
     for (int s = 0; s < S::kKSD; ++s) {
       bf16x8 a[S::kKT];
 #pragma unroll
-      for (int t = 0; t < S::kKT; ++t) {
-        const int r = 32 * t + col;
-        a[t] = *reinterpret_cast<const bf16x8*>(kt + r * (2 * D) + (((2 * s + hl) ^ swz<S::kCprK>(r)) * 16));
-      }
+      for (int t = 0; t < S::kKT; ++t)
+        a[t] = *reinterpret_cast<const bf16x8*>(kt + t * (32 * 2 * D) + klane[s]);
 #pragma unroll
       for (int t = 0; t < S::kKT; ++t) sacc[t] = mfma32(a[t], qf[s], sacc[t]);
     }
@@ -286,7 +301,11 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[t][r]);
     const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(mx), __float_as_uint(mx), false, false);
-    return fmaxf(__uint_as_float(sw[0]), __uint_as_float(sw[1])) * scale_log2;
+    // scores are never NaN: a plain v_max, without the quieting moves the
+    // compiler adds to a max of values taken from another lane
+    float m2;
+    asm("v_max_f32 %0, %1, %2" : "=v"(m2) : "v"(__uint_as_float(sw[0])), "v"(__uint_as_float(sw[1])));
+    return m2 * scale_log2;
   };
   // lazy rescale: move the reference maximum only when the sub-tile's
   // maximum exceeds it by more than 2^8
@@ -318,11 +337,10 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
     }
 #pragma unroll
     for (int dt = 0; dt < S::kDT; ++dt) {
-      const int r = 32 * dt + col;
       bf16x8 a[S::kKSK];
 #pragma unroll
       for (int w = 0; w < S::kKSK; ++w)
-        a[w] = *reinterpret_cast<const bf16x8*>(vs + r * (2 * KS) + (((2 * w + hl) ^ swz<S::kCprV>(r)) * 16));
+        a[w] = *reinterpret_cast<const bf16x8*>(vs + dt * (32 * 2 * KS) + vlane[w]);
 #pragma unroll
       for (int w = 0; w < S::kKSK; ++w) oacc[dt] = mfma32(a[w], pb[w], oacc[dt]);
     }
