@@ -21,6 +21,9 @@ that definition:
   abstract; HEART abstract), plus RAPID's Turbo re-selection on cached scores.
 * ``retrieval`` - block retrieval accuracy: each query block's dense attention
   mass per key block, and the mass a selection captures (PARK, Abstract).
+* ``clustering`` - PARK's query-aware key clustering: k-means in the metric
+  the current queries induce, clusters as key blocks, their scores and
+  attention (PARK, Abstract).
 * ``correction`` - the cached correction of sparse attention by the attention
   over its omitted blocks, weighted by the fresh sparse statistics (RECAP
   abstract).
@@ -37,6 +40,8 @@ from .drift import drift, refresh_decision
 from .trajectory import cache_trajectory, turbo_schedule
 from .retrieval import captured_mass, dense_block_mass
 from .correction import complement_lists, corrected_trajectory, merge_partial, omitted_attention
+from .clustering import (assign, cluster_attention, cluster_keys, cluster_order, cluster_scores, kmeans,
+                         metric_distance, query_gram, update)
 
 __all__ = [
     "block_bounds", "num_blocks", "pool_keys", "score_blocks", "score_head",
@@ -44,4 +49,6 @@ __all__ = [
     "block_sparse_attention", "token_mask", "drift", "refresh_decision",
     "cache_trajectory", "turbo_schedule", "dense_block_mass", "captured_mass",
     "complement_lists", "omitted_attention", "merge_partial", "corrected_trajectory",
+    "query_gram", "metric_distance", "assign", "update", "kmeans", "cluster_order", "cluster_keys",
+    "cluster_scores", "cluster_attention",
 ]

@@ -568,3 +568,162 @@ def test_corrected_trajectory_refresh_is_dense_and_v_change_is_closed_form():
             vmix = np.where(kept[:, None], v1[a], v0[a])
             want = _sdpa(q[a, lo:hi], k[a], vmix)
             np.testing.assert_allclose(out[a, lo:hi], want, atol=1e-13)
+
+
+# ------------------------------------------------- query-aware key clustering
+
+def _sk_lloyd(x, init, iters):
+    """scikit-learn's Lloyd k-means from fixed initial centres (a library
+    implementation independent of the oracle)."""
+    from sklearn.cluster import KMeans
+    km = KMeans(n_clusters=init.shape[0], init=init, n_init=1, max_iter=iters, algorithm="lloyd", tol=0.0)
+    km.fit(x)
+    return km.cluster_centers_, km.labels_
+
+
+def _clustered_keys(n, d, nb, seed, spread=0.25):
+    """Keys drawn around nb well separated centres, the centres visited in
+    contiguous runs so the contiguous block means start near them."""
+    rng = np.random.default_rng(seed)
+    centres = rng.standard_normal((nb, d)) * 3.0
+    owner = np.minimum(np.arange(n) * nb // n, nb - 1)
+    return centres[owner] + spread * rng.standard_normal((n, d))
+
+
+def test_metric_distance_is_mean_squared_score_gap():
+    q = _rand((50, 6), 120)
+    k = _rand((10, 6), 121)
+    c = _rand(6, 122)
+    g = O.query_gram(q)
+    want = ((q @ k.T - (q @ c)[:, None]) ** 2).mean(axis=0)
+    np.testing.assert_allclose(O.metric_distance(k, c, g), want, rtol=1e-12)
+
+
+def test_kmeans_identity_metric_is_lloyd():
+    """Queries whose Gram matrix is the identity: plain Euclidean k-means,
+    checked against scikit-learn's Lloyd iterations from the same start."""
+    n, d, b = 120, 4, 20
+    q = np.sqrt(d) * np.eye(d)[np.arange(n) % d]
+    np.testing.assert_allclose(O.query_gram(q), np.eye(d), atol=1e-15)
+    k = _clustered_keys(n, d, n // b, 123, spread=1.5)
+    for iters in (1, 3, 8):
+        labels, cents, sizes = O.kmeans(k, O.query_gram(q), b, iters)
+        sk_c, sk_l = _sk_lloyd(k, O.pool_keys(k, b), iters)
+        np.testing.assert_allclose(cents, sk_c, atol=1e-12)
+        assert (sizes == np.bincount(labels, minlength=n // b)).all()
+    # the library's final labels are the assignment to its final centres
+    assert (O.assign(k, cents, np.eye(d))[0] == sk_l).all()
+
+
+def test_kmeans_query_metric_is_euclidean_on_transformed_keys():
+    """G = L L^T: the query metric is Euclidean distance between keys mapped
+    by x -> x L, so scikit-learn on the mapped keys reproduces it."""
+    n, d, b = 150, 5, 25
+    mix = _rand((d, d), 124)
+    q = _rand((300, d), 125) @ mix
+    g = O.query_gram(q)
+    L = np.linalg.cholesky(g)
+    k = _clustered_keys(n, d, n // b, 126, spread=1.0)
+    for iters in (1, 4):
+        labels, cents, _ = O.kmeans(k, g, b, iters)
+        sk_c, sk_l = _sk_lloyd(k @ L, O.pool_keys(k, b) @ L, iters)
+        np.testing.assert_allclose(cents @ L, sk_c, atol=1e-10)
+    assert (O.assign(k, cents, g)[0] == sk_l).all()
+
+
+def test_query_aware_clusters_group_equal_scores():
+    """Queries that only see coordinate 0: keys differ there by sign and
+    elsewhere by large noise.  The query metric splits the keys by sign, so
+    every cluster's keys get identical scores from every query; Euclidean
+    clustering splits by the noise instead."""
+    rng = np.random.default_rng(127)
+    n, d = 200, 8
+    q = np.zeros((60, d))
+    q[:, 0] = rng.uniform(0.5, 2.0, 60)
+    sign = np.where(np.arange(n) < n // 2, rng.random(n) < 0.7, rng.random(n) < 0.3)
+    k = 3.0 * rng.standard_normal((n, d))
+    k[:, 0] = np.where(sign, 1.0, -1.0)
+    labels, _, _ = O.kmeans(k, O.query_gram(q), n // 2, 3)
+    assert (labels == np.where(sign, 0, 1)).all()
+    for j in (0, 1):
+        scores = q @ k[labels == j].T
+        assert np.ptp(scores, axis=1).max() == 0.0
+    eu, _, _ = O.kmeans(k, np.eye(d), n // 2, 3)
+    assert (eu != labels).mean() > 0.1
+
+
+def test_kmeans_objective_never_increases():
+    k = _rand((90, 4), 128)
+    q = _rand((40, 4), 129)
+    g = O.query_gram(q)
+    prev = np.inf
+    c = O.pool_keys(k, 10)
+    for _ in range(6):
+        labels, dist = O.assign(k, c, g)
+        obj = dist[np.arange(90), labels].sum()
+        assert obj <= prev + 1e-12
+        prev = obj
+        c, _ = O.update(k, labels, c)
+        # assignment is optimal for the centroids it saw
+        assert (dist[np.arange(90), labels] <= dist.min(axis=1) + 0.0).all()
+
+
+def test_update_means_and_empty_cluster():
+    k = _rand((7, 3), 130)
+    labels = np.array([2, 0, 2, 2, 0, 3, 3], np.int32)
+    c0 = _rand((4, 3), 131)
+    c, sizes = O.update(k, labels, c0)
+    assert sizes.tolist() == [2, 0, 3, 2]
+    np.testing.assert_allclose(c[0], (k[1] + k[4]) / 2, rtol=1e-15)
+    np.testing.assert_allclose(c[2], (k[0] + k[2] + k[3]) / 3, rtol=1e-15)
+    assert (c[1] == c0[1]).all()
+
+
+def test_cluster_order_is_stable_sort():
+    labels = np.array([3, 1, 3, 0, 1, 1, 3, 0], np.int32)
+    assert O.cluster_order(labels).tolist() == [3, 7, 1, 4, 5, 0, 2, 6]
+
+
+def test_contiguous_clusters_reduce_to_park_blocks():
+    """Clusters that are the contiguous blocks: cluster scores are PARK's
+    block scores and cluster attention is block-sparse attention."""
+    n, b, d = 45, 8, 5
+    q, k, v = (_rand((n, d), 132 + i, 0.8) for i in range(3))
+    nb = O.num_blocks(n, b)
+    labels = (np.arange(n) // b).astype(np.int32)
+    cents, sizes = O.update(k, labels, np.zeros((nb, d)))
+    np.testing.assert_allclose(cents, O.pool_keys(k, b), rtol=1e-14)
+    s = 1 / np.sqrt(d)
+    np.testing.assert_allclose(O.cluster_scores(q, cents, sizes, b), O.score_head(q, k, b, s), atol=1e-15)
+    rng = np.random.default_rng(135)
+    lists = [rng.choice(nb, int(rng.integers(0, nb + 1)), replace=False) for _ in range(nb)]
+    o1, l1 = O.cluster_attention(q, k, v, b, labels, lists)
+    o2, l2 = O.block_sparse_attention(q, k, v, b, lists)
+    np.testing.assert_allclose(o1, o2, atol=1e-14)
+    np.testing.assert_allclose(l1, l2, atol=1e-13)       # -inf rows match as -inf
+
+
+def test_cluster_scores_skip_empty_clusters():
+    n, b, d = 40, 8, 4
+    q, k = _rand((n, d), 136), _rand((n, d), 137)
+    labels = np.array([0, 2, 3, 4] * 10, np.int32)            # cluster 1 is empty
+    cents, sizes = O.update(k, labels, _rand((5, d), 138))
+    sc = O.cluster_scores(q, cents, sizes, b)
+    assert (sc[:, 1] == 0).all()
+    np.testing.assert_allclose(sc.sum(axis=1), 1.0, rtol=1e-14)
+    live = [0, 2, 3, 4]
+    want = _sdpa(q, cents[live], np.eye(4), scale=1 / np.sqrt(d))
+    np.testing.assert_allclose(sc[:, live], np.stack([want[i * b:(i + 1) * b].mean(0) for i in range(5)]),
+                               atol=1e-14)
+
+
+def test_cluster_attention_full_selection_is_dense():
+    n, b, d = 37, 8, 4
+    q, k, v = (_rand((n, d), 139 + i) for i in range(3))
+    labels = np.random.default_rng(142).integers(0, 5, n).astype(np.int32)
+    out, lse = O.cluster_attention(q, k, v, b, labels, [list(range(5))] * 5)
+    np.testing.assert_allclose(out, _sdpa(q, k, v), atol=1e-13)
+    sel = [[1, 3]] * 5
+    out, _ = O.cluster_attention(q, k, v, b, labels, sel)
+    mask = np.isin(labels, [1, 3])[None, :].repeat(n, 0)
+    np.testing.assert_allclose(out, _sdpa(q, k, v, mask=mask), atol=1e-13)
