@@ -9,15 +9,15 @@ two attentions over disjoint key sets).  This package is only their ctypes
 binding plus the host loop that reuses cached masks across denoising steps.
 """
 from .binding import (Problem, RsaError, RsaLibraryMissing, attn_merge, attn_omitted,
-                      block_sparse_attn, declared_functions,
+                      block_sparse_attn, declared_functions, kmeans, query_gram,
                       dense_block_mass, lib, make_problem, mask_drift, score_blocks,
                       score_blocks_pooled, select_topp, workspace_bytes, OP_ATTN, OP_DRIFT,
-                      OP_POOLED, OP_SCORE, OP_SELECT, RSA_BF16, RSA_FP32, LIB_PATH)
+                      OP_GRAM, OP_KMEANS, OP_POOLED, OP_SCORE, OP_SELECT, RSA_BF16, RSA_FP32, LIB_PATH)
 from .cache import MaskCache
 
 __all__ = [
     "Problem", "RsaError", "RsaLibraryMissing", "attn_merge", "attn_omitted", "block_sparse_attn",
-    "declared_functions",
+    "declared_functions", "kmeans", "query_gram", "OP_GRAM", "OP_KMEANS",
     "dense_block_mass", "lib", "make_problem", "mask_drift", "score_blocks", "score_blocks_pooled",
     "select_topp", "workspace_bytes", "MaskCache", "OP_ATTN", "OP_DRIFT", "OP_POOLED", "OP_SCORE",
     "OP_SELECT", "RSA_BF16", "RSA_FP32", "LIB_PATH",

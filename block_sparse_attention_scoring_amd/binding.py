@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "lib", "librsa.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "rsa.h")
 
 RSA_BF16, RSA_FP32 = 0, 1
-OP_SCORE, OP_SELECT, OP_DRIFT, OP_ATTN, OP_POOLED = 0, 1, 2, 3, 4
+OP_SCORE, OP_SELECT, OP_DRIFT, OP_ATTN, OP_POOLED, OP_GRAM, OP_KMEANS = 0, 1, 2, 3, 4, 5, 6
 
 
 class RsaLibraryMissing(RuntimeError):
@@ -75,6 +75,8 @@ def _declare(lib):
         "rsa_score_blocks_pooled": (i32, [pp, _P, _P, _P, _P, sz, _P]),
         "rsa_attn_omitted": (i32, [pp, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
         "rsa_attn_merge": (i32, [pp, _P, _P, _P, _P, _P]),
+        "rsa_query_gram": (i32, [pp, _P, _P, _P, sz, _P]),
+        "rsa_kmeans": (i32, [pp, _P, _P, i32, i32, _P, _P, _P, _P, _P, sz, _P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -242,3 +244,33 @@ def attn_merge(out, lse, part_out, part_lse, p: Problem):
     _check(lib().rsa_attn_merge(ctypes.byref(p), _ptr(out), _ptr(lse), _ptr(part_out), _ptr(part_lse),
                                 _stream(out)), "rsa_attn_merge")
     return out, lse
+
+
+def query_gram(q, p: Problem, out=None, workspace=None):
+    """Gram matrix of the current queries, [heads, head_dim, head_dim] fp32 (rsa_query_gram)."""
+    if out is None:
+        out = torch.empty((p.heads, p.head_dim, p.head_dim), dtype=torch.float32, device=q.device)
+    ws, wsb = _workspace(p, OP_GRAM, q.device, workspace)
+    _check(lib().rsa_query_gram(ctypes.byref(p), _ptr(q), _ptr(out), _ptr(ws), wsb, _stream(q)), "rsa_query_gram")
+    return out
+
+
+def kmeans(k, gram, p: Problem, iters: int, init: bool = True, centroids=None, labels=None, sizes=None,
+           order=None, workspace=None):
+    """Lloyd k-means of the keys in the metric of ``gram`` (rsa_kmeans)
+    -> (centroids fp32 [H, NB, D], labels i32 [H, N], sizes i32 [H, NB], order i32 [H, N])."""
+    nb, dev = p.nblocks, k.device
+    if centroids is None:
+        if not init:
+            raise ValueError("kmeans without init needs starting centroids")
+        centroids = torch.empty((p.heads, nb, p.head_dim), dtype=torch.float32, device=dev)
+    if labels is None:
+        labels = torch.empty((p.heads, p.tokens), dtype=torch.int32, device=dev)
+    if sizes is None:
+        sizes = torch.empty((p.heads, nb), dtype=torch.int32, device=dev)
+    if order is None:
+        order = torch.empty((p.heads, p.tokens), dtype=torch.int32, device=dev)
+    ws, wsb = _workspace(p, OP_KMEANS, dev, workspace)
+    _check(lib().rsa_kmeans(ctypes.byref(p), _ptr(k), _ptr(gram), int(iters), int(bool(init)), _ptr(centroids),
+                            _ptr(labels), _ptr(sizes), _ptr(order), _ptr(ws), wsb, _stream(k)), "rsa_kmeans")
+    return centroids, labels, sizes, order

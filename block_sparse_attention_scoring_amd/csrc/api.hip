@@ -7,7 +7,7 @@
 
 namespace {
 
-constexpr int kMaxBlocks = 4096;
+constexpr int kMaxBlocks = rsa::kMaxClusters;
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 bool aligned256(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 255u) == 0; }
@@ -46,6 +46,8 @@ size_t ws_bytes_for(const rsa::Problem& p, int op) {
     case RSA_OP_DRIFT: return rsa::drift_ws_bytes(p);
     case RSA_OP_ATTN: return rsa::attn_ws_bytes(p);
     case RSA_OP_POOLED: return rsa::pooled_ws_bytes(p);
+    case RSA_OP_GRAM: return rsa::gram_ws_bytes(p);
+    case RSA_OP_KMEANS: return rsa::kmeans_ws_bytes(p);
     default: return 0;
   }
 }
@@ -197,6 +199,34 @@ rsa_status rsa_attn_merge(const rsa_problem* p, void* out, float* lse, const voi
     return RSA_ERR_NULL;
   if (!aligned16(out) || !aligned16(part_out)) return RSA_ERR_ALIGN;
   return hip_status(rsa::launch_merge(pr, out, lse, part_out, part_lse, stream));
+}
+
+rsa_status rsa_query_gram(const rsa_problem* p, const void* q, float* gram, void* ws, size_t ws_bytes,
+                          hipStream_t stream) {
+  rsa::Problem pr;
+  rsa_status st = make_problem(p, &pr);
+  if (st != RSA_OK) return st;
+  if (q == nullptr || gram == nullptr) return RSA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(gram)) return RSA_ERR_ALIGN;
+  st = check_ws(pr, RSA_OP_GRAM, ws, ws_bytes);
+  if (st != RSA_OK) return st;
+  return hip_status(rsa::launch_gram(pr, q, gram, ws, stream));
+}
+
+rsa_status rsa_kmeans(const rsa_problem* p, const void* k, const float* gram, int32_t iters, int32_t init,
+                      float* centroids, int32_t* labels, int32_t* sizes, int32_t* order, void* ws,
+                      size_t ws_bytes, hipStream_t stream) {
+  rsa::Problem pr;
+  rsa_status st = make_problem(p, &pr);
+  if (st != RSA_OK) return st;
+  if (k == nullptr || gram == nullptr || centroids == nullptr || labels == nullptr || sizes == nullptr ||
+      order == nullptr)
+    return RSA_ERR_NULL;
+  if (iters < 1 || iters > 1000) return RSA_ERR_ARG;
+  if (!aligned16(k) || !aligned16(centroids)) return RSA_ERR_ALIGN;
+  st = check_ws(pr, RSA_OP_KMEANS, ws, ws_bytes);
+  if (st != RSA_OK) return st;
+  return hip_status(rsa::launch_kmeans(pr, k, gram, iters, init != 0, centroids, labels, sizes, order, ws, stream));
 }
 
 }  // extern "C"

@@ -1,0 +1,493 @@
+// Query-aware key clustering (gfx950).
+//
+// PARK (Accurate Block Retrieval for Sparse Attention in Video Diffusion
+// Transformers), Abstract: keys are transformed with information from the
+// current queries before clustering, so that keys the queries score alike are
+// grouped, and the clusters' mean representations drive block retrieval.
+//
+// The metric is the one the current queries induce: G = Q^T Q / N, and the
+// squared distance of a key k to a centroid c is (k - c)^T G (k - c), the
+// mean over the queries of the squared gap between their scores of k and c.
+//
+//   gram:   per chunk of tokens a partial Q^T Q (bf16: 32x32x16 matrix-core
+//           products of exact bf16 values, fp32 sums), then the chunks added
+//           in a fixed order in fp64 and divided by N.
+//   k-means iteration (Lloyd):
+//     wprep   W_j = 2 G c_j and b_j = c_j^T G c_j for every centroid; W split
+//             into two bf16 terms (16 significant bits) for the matrix cores;
+//     assign  the nearest centroid maximises 2 k.G c_j - c_j^T G c_j: one
+//             workgroup per 128 keys, the keys in registers, centroid chunks of
+//             32 streamed through LDS, a running maximum per key (ties: the
+//             lower cluster index);
+//     sort    a stable counting sort of the keys by cluster (per-chunk
+//             histograms and in-chunk ranks, a scan over chunks and clusters,
+//             a scatter), deterministic, no floating-point atomics;
+//     means   each non-empty cluster's centroid = mean of its keys in sorted
+//             order (fp64 sums, one rounding); an empty cluster keeps its own.
+#include "common.h"
+#include "kernels.h"
+
+namespace rsa {
+namespace {
+
+constexpr int kGramChunk = 2048;  // tokens per partial Gram matrix
+constexpr int kGramStage = 64;    // tokens staged in LDS at a time
+constexpr int kHistChunk = 256;   // tokens per histogram chunk
+constexpr int kAssignRows = 128;  // keys per assignment workgroup
+
+// ---------------------------------------------------------------- gram
+// Partial Q^T Q of one chunk of kGramChunk tokens, bf16 input.  The chunk is
+// staged 64 tokens at a time in LDS transposed (dim-major), so that both
+// operands of a 32x32x16 product (8 consecutive tokens of one dim per lane)
+// are single 16-byte reads.  Wave w owns output tiles w*kPerWave.. of the
+// (D/32)^2 tiles of G.
+template <int D>
+__global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t* __restrict__ q,
+                                                        float* __restrict__ part, int N, int nchunk) {
+  constexpr int kT = D / 32;                // tiles per side
+  constexpr int kPerWave = kT * kT / 4;     // tiles per wave
+  constexpr int kStride = kGramStage + 8;   // LDS row pitch in tokens (bank spread)
+  __shared__ __attribute__((aligned(16))) uint16_t qt[D * kStride];
+  const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6, hl = lane >> 5, col = lane & 31;
+  const int t0 = c * kGramChunk, t1 = min(N, t0 + kGramChunk);
+  const uint16_t* qh = q + static_cast<size_t>(h) * N * D;
+  f32x16 acc[kPerWave];
+#pragma unroll
+  for (int i = 0; i < kPerWave; ++i) acc[i] = f32x16{};
+  for (int s0 = t0; s0 < t1; s0 += kGramStage) {
+    __syncthreads();
+    for (int e = tid; e < kGramStage * D / 8; e += 256) {
+      const int t = e / (D / 8), d8 = (e % (D / 8)) * 8;
+      u32x4 x = s0 + t < t1 ? *reinterpret_cast<const u32x4*>(qh + static_cast<size_t>(s0 + t) * D + d8)
+                            : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        qt[(d8 + 2 * w) * kStride + t] = static_cast<uint16_t>(x[w] & 0xffffu);
+        qt[(d8 + 2 * w + 1) * kStride + t] = static_cast<uint16_t>(x[w] >> 16);
+      }
+    }
+    __syncthreads();
+#pragma unroll
+    for (int ks = 0; ks < kGramStage / 16; ++ks) {
+      const int tk = ks * 16 + 8 * hl;
+#pragma unroll
+      for (int i = 0; i < kPerWave; ++i) {
+        const int tile = wave * kPerWave + i, ti = tile / kT, tj = tile % kT;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(&qt[(32 * ti + col) * kStride + tk]);
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(&qt[(32 * tj + col) * kStride + tk]);
+        acc[i] = mfma32(a, b, acc[i]);
+      }
+    }
+  }
+  float* dst = part + (static_cast<size_t>(h) * nchunk + c) * D * D;
+#pragma unroll
+  for (int i = 0; i < kPerWave; ++i) {
+    const int tile = wave * kPerWave + i, ti = tile / kT, tj = tile % kT;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) dst[(32 * ti + acc_row(r, hl)) * D + 32 * tj + col] = acc[i][r];
+  }
+}
+
+// fp32 input: one thread per entry of G, fp64 sum over all tokens (the
+// correctness path of fp32 problems, which are small).
+template <int D>
+__global__ __launch_bounds__(256) void gram_f32_kernel(const float* __restrict__ q, float* __restrict__ gram,
+                                                       int N) {
+  const int h = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= D * D) return;
+  const int a = e / D, b = e % D;
+  const float* qh = q + static_cast<size_t>(h) * N * D;
+  double s = 0.0;
+  for (int t = 0; t < N; ++t) s += static_cast<double>(qh[static_cast<size_t>(t) * D + a]) * qh[static_cast<size_t>(t) * D + b];
+  gram[static_cast<size_t>(h) * D * D + e] = static_cast<float>(s / N);
+}
+
+// G = (sum of the chunks' partials, in chunk order, fp64) / N.
+template <int D>
+__global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restrict__ part, float* __restrict__ gram,
+                                                          int N, int nchunk) {
+  const int h = blockIdx.y, e = blockIdx.x * 256 + threadIdx.x;
+  if (e >= D * D) return;
+  const float* p = part + static_cast<size_t>(h) * nchunk * D * D + e;
+  double s = 0.0;
+  for (int c = 0; c < nchunk; ++c) s += p[static_cast<size_t>(c) * D * D];
+  gram[static_cast<size_t>(h) * D * D + e] = static_cast<float>(s / N);
+}
+
+// ---------------------------------------------------------------- wprep
+// For 32 centroids per workgroup: W_j = 2 G c_j (fp32, e ascending), split
+// into bf16 hi + lo, and b_j = c_j . (G c_j).  Rows past NB get zero W and
+// b = +inf, so they never win the assignment.
+template <int D>
+__global__ __launch_bounds__(256) void wprep_kernel(const float* __restrict__ gram, const float* __restrict__ cent,
+                                                    uint16_t* __restrict__ whi, uint16_t* __restrict__ wlo,
+                                                    float* __restrict__ w32, float* __restrict__ bvec, int NB,
+                                                    int NBp) {
+  __shared__ float cs[32][D];
+  __shared__ float ws[32][D + 1];
+  const int j0 = blockIdx.x * 32, h = blockIdx.y, tid = threadIdx.x;
+  const float* g = gram + static_cast<size_t>(h) * D * D;  // read by rows: neighbouring threads, neighbouring d
+  for (int e = tid; e < 32 * D; e += 256) {
+    const int j = e / D, d = e % D;
+    cs[j][d] = j0 + j < NB ? cent[(static_cast<size_t>(h) * NB + j0 + j) * D + d] : 0.f;
+  }
+  __syncthreads();
+  for (int e = tid; e < 32 * D; e += 256) {
+    const int j = e / D, d = e % D;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int x = 0; x < D; ++x) acc = fmaf(g[x * D + d], cs[j][x], acc);  // G symmetric: G[d][x] = G[x][d]
+    ws[j][d] = acc;
+    const float w2 = 2.f * acc;
+    const __bf16 hi = static_cast<__bf16>(w2);
+    const __bf16 lo = static_cast<__bf16>(w2 - static_cast<float>(hi));
+    const size_t o = (static_cast<size_t>(h) * NBp + j0 + j) * D + d;
+    whi[o] = __builtin_bit_cast(uint16_t, hi);
+    wlo[o] = __builtin_bit_cast(uint16_t, lo);
+    w32[o] = w2;
+  }
+  __syncthreads();
+  if (tid < 32) {
+    float b = 0.f;
+    for (int d = 0; d < D; ++d) b = fmaf(cs[tid][d], ws[tid][d], b);
+    bvec[static_cast<size_t>(h) * NBp + j0 + tid] = j0 + tid < NB ? b : INFINITY;
+  }
+}
+
+// ---------------------------------------------------------------- assign
+// One workgroup per 128 keys (4 waves of 32).  Each lane holds its key's
+// dims 16s + 8hl..+7 in registers (bf16, exact).  Centroid chunks of 32
+// (W hi and lo tiles, swizzled) go through LDS; S^T = W K^T puts the 16
+// clusters 32c + acc_row(r, hl) of this lane's key in its registers, so the
+// running maximum of 2 k.G c_j - b_j stays in-lane; the halves merge last.
+template <int D>
+__global__ __launch_bounds__(256) void assign_bf16_kernel(const uint16_t* __restrict__ k,
+                                                          const uint16_t* __restrict__ whi,
+                                                          const uint16_t* __restrict__ wlo,
+                                                          const float* __restrict__ bvec,
+                                                          int* __restrict__ labels, int N, int NBp) {
+  constexpr int kKS = D / 16, kCpr = D / 8;
+  __shared__ __attribute__((aligned(16))) uint16_t th[32 * D];
+  __shared__ __attribute__((aligned(16))) uint16_t tl[32 * D];
+  __shared__ float bs[32];
+  const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int hl = lane >> 5, col = lane & 31;
+  const int t = blockIdx.x * kAssignRows + wave * 32 + col;
+  bf16x8 kf[kKS];
+  {
+    const bool ok = t < N;
+    const u32x4* src = reinterpret_cast<const u32x4*>(k + (static_cast<size_t>(h) * N + (ok ? t : 0)) * D);
+#pragma unroll
+    for (int s = 0; s < kKS; ++s) kf[s] = __builtin_bit_cast(bf16x8, ok ? src[2 * s + hl] : u32x4{0, 0, 0, 0});
+  }
+  const uint16_t* wh = whi + static_cast<size_t>(h) * NBp * D;
+  const uint16_t* wl = wlo + static_cast<size_t>(h) * NBp * D;
+  float best = -INFINITY;
+  int bj = 0;
+  for (int c = 0; c < NBp / 32; ++c) {
+    __syncthreads();
+    for (int e = tid; e < 32 * kCpr; e += 256) {
+      const int r = e / kCpr, ch = e % kCpr;
+      const size_t g = (static_cast<size_t>(32 * c + r) * D) + ch * 8;
+      const int dst = r * D + (ch ^ swz<kCpr>(r)) * 8;
+      *reinterpret_cast<u32x4*>(&th[dst]) = *reinterpret_cast<const u32x4*>(wh + g);
+      *reinterpret_cast<u32x4*>(&tl[dst]) = *reinterpret_cast<const u32x4*>(wl + g);
+    }
+    if (tid < 32) bs[tid] = bvec[static_cast<size_t>(h) * NBp + 32 * c + tid];
+    __syncthreads();
+    f32x16 ah = f32x16{}, al = f32x16{};
+#pragma unroll
+    for (int s = 0; s < kKS; ++s) {
+      const int o = col * D + ((2 * s + hl) ^ swz<kCpr>(col)) * 8;
+      ah = mfma32(*reinterpret_cast<const bf16x8*>(&th[o]), kf[s], ah);
+      al = mfma32(*reinterpret_cast<const bf16x8*>(&tl[o]), kf[s], al);
+    }
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const int jr = acc_row(r, hl);
+      const float v = (ah[r] + al[r]) - bs[jr];
+      if (v > best) {  // rows ascend with r: the first maximum is the lowest index
+        best = v;
+        bj = 32 * c + jr;
+      }
+    }
+  }
+  const float ob = __shfl_xor(best, 32);
+  const int oj = __shfl_xor(bj, 32);
+  if (ob > best || (ob == best && oj < bj)) bj = oj;
+  if (hl == 0 && t < N) labels[static_cast<size_t>(h) * N + t] = bj;
+}
+
+// fp32 keys: one thread per key, fp64 dot products with the fp32 W.
+template <int D>
+__global__ __launch_bounds__(256) void assign_f32_kernel(const float* __restrict__ k, const float* __restrict__ w32,
+                                                         const float* __restrict__ bvec, int* __restrict__ labels,
+                                                         int N, int NB, int NBp) {
+  const int h = blockIdx.y, t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= N) return;
+  const float* kr = k + (static_cast<size_t>(h) * N + t) * D;
+  double best = -INFINITY;
+  int bj = 0;
+  for (int j = 0; j < NB; ++j) {
+    const float* w = w32 + (static_cast<size_t>(h) * NBp + j) * D;
+    double s = 0.0;
+    for (int d = 0; d < D; ++d) s += static_cast<double>(kr[d]) * w[d];
+    const double v = s - bvec[static_cast<size_t>(h) * NBp + j];
+    if (v > best) {
+      best = v;
+      bj = j;
+    }
+  }
+  labels[static_cast<size_t>(h) * N + t] = bj;
+}
+
+// ---------------------------------------------------------------- sort
+// Per chunk of 256 keys: the count of every cluster in the chunk and each
+// key's rank among the chunk's earlier keys of its cluster.
+__global__ __launch_bounds__(kHistChunk) void hist_kernel(const int* __restrict__ labels, int* __restrict__ hist,
+                                                          int* __restrict__ rank, int N, int NB, int nch) {
+  __shared__ int lab[kHistChunk];
+  __shared__ int cnt[kMaxClusters];
+  const int ch = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int t = ch * kHistChunk + tid;
+  const int my = t < N ? labels[static_cast<size_t>(h) * N + t] : -1;
+  lab[tid] = my;
+  for (int j = tid; j < NB; j += kHistChunk) cnt[j] = 0;
+  __syncthreads();
+  if (my >= 0) {
+    int r = 0;
+    for (int i = 0; i < tid; ++i) r += lab[i] == my;
+    rank[static_cast<size_t>(h) * N + t] = r;
+    atomicAdd(&cnt[my], 1);  // integer counts: the same for every order
+  }
+  __syncthreads();
+  int* dst = hist + (static_cast<size_t>(h) * nch + ch) * NB;
+  for (int j = tid; j < NB; j += kHistChunk) dst[j] = cnt[j];
+}
+
+// Per head: turn the chunk histograms into each chunk's first rank per
+// cluster (exclusive over chunks, in place), the cluster sizes, and each
+// cluster's first position in the sorted order (exclusive over clusters).
+__global__ __launch_bounds__(256) void scan_kernel(int* __restrict__ hist, int* __restrict__ sizes,
+                                                   int* __restrict__ offs, int NB, int nch) {
+  __shared__ int sz[kMaxClusters];
+  __shared__ int part[256];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  for (int j = tid; j < NB; j += 256) {
+    int run = 0;
+    for (int c = 0; c < nch; ++c) {
+      int* p = hist + (static_cast<size_t>(h) * nch + c) * NB + j;
+      const int v = *p;
+      *p = run;
+      run += v;
+    }
+    sz[j] = run;
+    sizes[static_cast<size_t>(h) * NB + j] = run;
+  }
+  __syncthreads();
+  constexpr int kPer = kMaxClusters / 256;  // clusters per thread in the scan
+  int local = 0;
+  for (int e = 0; e < kPer; ++e) {
+    const int j = tid * kPer + e;
+    if (j < NB) local += sz[j];
+  }
+  part[tid] = local;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int v = part[i];
+      part[i] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  int run = part[tid];
+  for (int e = 0; e < kPer; ++e) {
+    const int j = tid * kPer + e;
+    if (j < NB) {
+      offs[static_cast<size_t>(h) * NB + j] = run;
+      run += sz[j];
+    }
+  }
+}
+
+// order[first(cluster) + first rank of this chunk + rank in chunk] = key.
+__global__ __launch_bounds__(kHistChunk) void scatter_kernel(const int* __restrict__ labels,
+                                                             const int* __restrict__ hist,
+                                                             const int* __restrict__ rank,
+                                                             const int* __restrict__ offs, int* __restrict__ order,
+                                                             int N, int NB, int nch) {
+  const int ch = blockIdx.x, h = blockIdx.y;
+  const int t = ch * kHistChunk + threadIdx.x;
+  if (t >= N) return;
+  const size_t ht = static_cast<size_t>(h) * N + t;
+  const int j = labels[ht];
+  const int pos = offs[static_cast<size_t>(h) * NB + j] + hist[(static_cast<size_t>(h) * nch + ch) * NB + j] + rank[ht];
+  order[static_cast<size_t>(h) * N + pos] = t;
+}
+
+// ---------------------------------------------------------------- means
+template <typename T>
+__device__ __forceinline__ void load8f(const T* src, float (&x)[8]);
+template <>
+__device__ __forceinline__ void load8f<uint16_t>(const uint16_t* src, float (&x)[8]) {
+  const u32x4 raw = *reinterpret_cast<const u32x4*>(src);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = __uint_as_float(raw[e] << 16);
+    x[2 * e + 1] = __uint_as_float(raw[e] & 0xffff0000u);
+  }
+}
+template <>
+__device__ __forceinline__ void load8f<float>(const float* src, float (&x)[8]) {
+  const f32x4 a = *reinterpret_cast<const f32x4*>(src);
+  const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = a[e];
+    x[4 + e] = b[e];
+  }
+}
+
+// One workgroup per (cluster, head): the mean of the cluster's keys, visited
+// in sorted order by 256/(D/8) row groups, fp64 sums added in group order.
+template <typename T, int D>
+__global__ __launch_bounds__(256) void means_kernel(const T* __restrict__ k, const int* __restrict__ order,
+                                                    const int* __restrict__ sizes, const int* __restrict__ offs,
+                                                    float* __restrict__ cent, int N, int NB) {
+  constexpr int kLanes = D / 8, kGroups = 256 / kLanes;
+  __shared__ double part[kGroups][D];
+  const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int n = sizes[static_cast<size_t>(h) * NB + j];
+  if (n == 0) return;  // an empty cluster keeps its centroid
+  const int* ord = order + static_cast<size_t>(h) * N + offs[static_cast<size_t>(h) * NB + j];
+  const int rg = tid / kLanes, c8 = (tid % kLanes) * 8;
+  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int r = rg; r < n; r += kGroups) {
+    float x[8];
+    load8f<T>(k + (static_cast<size_t>(h) * N + ord[r]) * D + c8, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[e] += static_cast<double>(x[e]);
+  }
+#pragma unroll
+  for (int e = 0; e < 8; ++e) part[rg][c8 + e] = acc[e];
+  __syncthreads();
+  if (tid < D) {
+    double s = 0.0;
+    for (int g = 0; g < kGroups; ++g) s += part[g][tid];
+    cent[(static_cast<size_t>(h) * NB + j) * D + tid] = static_cast<float>(s / n);
+  }
+}
+
+struct KmeansWs {
+  uint16_t *whi, *wlo;
+  float *w32, *bvec, *bmax;
+  int *hist, *rank, *offs;
+  size_t total;
+};
+
+size_t al256(size_t x) { return (x + 255) / 256 * 256; }
+
+KmeansWs kmeans_ws_layout(const Problem& p, void* base) {
+  const size_t NBp = (p.nb + 31) / 32 * 32;
+  const size_t nch = (p.tokens + kHistChunk - 1) / kHistChunk;
+  const size_t H = p.heads, D = p.head_dim;
+  const size_t sizes[] = {al256(2 * H * NBp * D), al256(2 * H * NBp * D), al256(4 * H * NBp * D),
+                          al256(4 * H * NBp), al256(4 * H * p.nb), al256(4 * H * nch * p.nb),
+                          al256(4 * H * static_cast<size_t>(p.tokens)), al256(4 * H * p.nb)};
+  KmeansWs w{};
+  char* b = static_cast<char*>(base);
+  size_t off = 0;
+  void** ptrs[] = {(void**)&w.whi, (void**)&w.wlo, (void**)&w.w32, (void**)&w.bvec,
+                   (void**)&w.bmax, (void**)&w.hist, (void**)&w.rank, (void**)&w.offs};
+  for (int i = 0; i < 8; ++i) {
+    if (b != nullptr) *ptrs[i] = b + off;
+    off += sizes[i];
+  }
+  w.total = off;
+  return w;
+}
+
+size_t gram_chunks(const Problem& p) { return (p.tokens + kGramChunk - 1) / kGramChunk; }
+
+template <int D>
+hipError_t launch_kmeans_t(const Problem& p, const void* k, const float* gram, int iters, int init, float* cent,
+                           int* labels, int* sizes, int* order, void* ws, hipStream_t stream) {
+  const KmeansWs w = kmeans_ws_layout(p, ws);
+  const int NB = p.nb, NBp = (p.nb + 31) / 32 * 32, N = p.tokens, H = p.heads;
+  const int nch = (N + kHistChunk - 1) / kHistChunk;
+  hipError_t e;
+  if (init) {
+    e = launch_block_means(p, k, 1.0, cent, w.bmax, stream);
+    if (e != hipSuccess) return e;
+  }
+  for (int it = 0; it < iters; ++it) {
+    hipLaunchKernelGGL((wprep_kernel<D>), dim3(NBp / 32, H), dim3(256), 0, stream, gram, cent, w.whi, w.wlo,
+                       w.w32, w.bvec, NB, NBp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (p.dtype == 0)
+      hipLaunchKernelGGL((assign_bf16_kernel<D>), dim3((N + kAssignRows - 1) / kAssignRows, H), dim3(256), 0,
+                         stream, static_cast<const uint16_t*>(k), w.whi, w.wlo, w.bvec, labels, N, NBp);
+    else
+      hipLaunchKernelGGL((assign_f32_kernel<D>), dim3((N + 255) / 256, H), dim3(256), 0, stream,
+                         static_cast<const float*>(k), w.w32, w.bvec, labels, N, NB, NBp);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(hist_kernel, dim3(nch, H), dim3(kHistChunk), 0, stream, labels, w.hist, w.rank, N, NB, nch);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(scan_kernel, dim3(H), dim3(256), 0, stream, w.hist, sizes, w.offs, NB, nch);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(scatter_kernel, dim3(nch, H), dim3(kHistChunk), 0, stream, labels, w.hist, w.rank, w.offs,
+                       order, N, NB, nch);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    if (p.dtype == 0)
+      hipLaunchKernelGGL((means_kernel<uint16_t, D>), dim3(NB, H), dim3(256), 0, stream,
+                         static_cast<const uint16_t*>(k), order, sizes, w.offs, cent, N, NB);
+    else
+      hipLaunchKernelGGL((means_kernel<float, D>), dim3(NB, H), dim3(256), 0, stream, static_cast<const float*>(k),
+                         order, sizes, w.offs, cent, N, NB);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
+template <int D>
+hipError_t launch_gram_t(const Problem& p, const void* q, float* gram, void* ws, hipStream_t stream) {
+  if (p.dtype != 0) {
+    hipLaunchKernelGGL((gram_f32_kernel<D>), dim3((D * D + 255) / 256, p.heads), dim3(256), 0, stream,
+                       static_cast<const float*>(q), gram, p.tokens);
+    return hipGetLastError();
+  }
+  const int nchunk = static_cast<int>(gram_chunks(p));
+  float* part = static_cast<float*>(ws);
+  hipLaunchKernelGGL((gram_bf16_kernel<D>), dim3(nchunk, p.heads), dim3(256), 0, stream,
+                     static_cast<const uint16_t*>(q), part, p.tokens, nchunk);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((gram_reduce_kernel<D>), dim3((D * D + 255) / 256, p.heads), dim3(256), 0, stream, part, gram,
+                     p.tokens, nchunk);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t gram_ws_bytes(const Problem& p) {
+  return p.dtype == 0 ? al256(sizeof(float) * p.heads * gram_chunks(p) * p.head_dim * p.head_dim) : 0;
+}
+
+hipError_t launch_gram(const Problem& p, const void* q, float* gram, void* ws, hipStream_t stream) {
+  return p.head_dim == 128 ? launch_gram_t<128>(p, q, gram, ws, stream) : launch_gram_t<64>(p, q, gram, ws, stream);
+}
+
+size_t kmeans_ws_bytes(const Problem& p) { return kmeans_ws_layout(p, nullptr).total; }
+
+hipError_t launch_kmeans(const Problem& p, const void* k, const float* gram, int iters, int init, float* cent,
+                         int* labels, int* sizes, int* order, void* ws, hipStream_t stream) {
+  return p.head_dim == 128
+             ? launch_kmeans_t<128>(p, k, gram, iters, init, cent, labels, sizes, order, ws, stream)
+             : launch_kmeans_t<64>(p, k, gram, iters, init, cent, labels, sizes, order, ws, stream);
+}
+
+}  // namespace rsa

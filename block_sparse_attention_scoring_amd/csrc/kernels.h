@@ -7,6 +7,8 @@
 
 namespace rsa {
 
+constexpr int kMaxClusters = 4096;  // largest number of blocks (and clusters) per sequence
+
 // Validated problem, derived sizes included.
 struct Problem {
   int heads, tokens, head_dim, block, nb;
@@ -63,5 +65,14 @@ hipError_t launch_dense_mass(const Problem& p, const void* q, const void* k, flo
 size_t pooled_ws_bytes(const Problem& p);
 hipError_t launch_pooled_scores(const Problem& p, const void* q, const void* k, float* scores,
                                 void* ws, hipStream_t stream);
+
+// Query-aware key clustering: G = Q^T Q / N per head (workspace: per-chunk
+// partial sums, bf16 only), and `iters` Lloyd iterations in the metric of G
+// (from the contiguous block means when `init` is set).
+size_t gram_ws_bytes(const Problem& p);
+hipError_t launch_gram(const Problem& p, const void* q, float* gram, void* ws, hipStream_t stream);
+size_t kmeans_ws_bytes(const Problem& p);
+hipError_t launch_kmeans(const Problem& p, const void* k, const float* gram, int iters, int init, float* cent,
+                         int* labels, int* sizes, int* order, void* ws, hipStream_t stream);
 
 }  // namespace rsa

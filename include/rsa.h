@@ -89,7 +89,9 @@ typedef enum {
   RSA_OP_SELECT = 1,
   RSA_OP_DRIFT = 2,
   RSA_OP_ATTN = 3,
-  RSA_OP_POOLED = 4 /* rsa_score_blocks_pooled */
+  RSA_OP_POOLED = 4, /* rsa_score_blocks_pooled */
+  RSA_OP_GRAM = 5,   /* rsa_query_gram */
+  RSA_OP_KMEANS = 6  /* rsa_kmeans */
 } rsa_op;
 
 /*
@@ -309,6 +311,49 @@ rsa_status rsa_attn_omitted(const rsa_problem* p, const void* q, const void* k, 
  */
 rsa_status rsa_attn_merge(const rsa_problem* p, void* out, float* lse, const void* part_out,
                           const float* part_lse, hipStream_t stream);
+
+/*
+ * Gram matrix of the current queries (PARK, Abstract: the keys are transformed
+ * with information from the current queries before they are clustered):
+ *
+ *   gram[h] = (1/N) sum_i q_i q_i^T,   [heads, head_dim, head_dim] fp32.
+ *
+ * It defines the metric of rsa_kmeans: (k - c)^T gram (k - c) is the mean over
+ * the current queries of the squared difference of their scores <q_i, k> and
+ * <q_i, c>.  q: [heads, tokens, head_dim] of `dtype`, 16-byte aligned; gram
+ * 16-byte aligned.  bf16: exact products on the matrix cores, fp32 sums per
+ * chunk of 2048 tokens, chunks added in fp64 in a fixed order; fp32: fp64
+ * sums.  ws / ws_bytes: at least rsa_workspace_bytes(p, RSA_OP_GRAM) bytes,
+ * 256-byte aligned (the chunks' partial sums; 0 bytes for fp32).
+ */
+rsa_status rsa_query_gram(const rsa_problem* p, const void* q, float* gram, void* ws, size_t ws_bytes,
+                          hipStream_t stream);
+
+/*
+ * Lloyd k-means of each head's keys in the metric of `gram` (PARK, Abstract:
+ * keys that receive similar query-key scores are grouped; the clusters are the
+ * key blocks).  NB = ceil(tokens / block) clusters.  With init != 0 the
+ * centroids first become the means of the contiguous key blocks; otherwise
+ * `centroids` holds the starting centroids.  Each of the `iters` iterations
+ * (1..1000) assigns every key to the centroid c_j minimising
+ * (k - c_j)^T gram (k - c_j) (ties: the lowest j), then moves every non-empty
+ * cluster's centroid to the mean of its keys; an empty cluster keeps its
+ * centroid.  Outputs, all for the last iteration:
+ *   centroids [heads, NB, head_dim] fp32 (in/out), 16-byte aligned;
+ *   labels    [heads, tokens] int32: each key's cluster;
+ *   sizes     [heads, NB] int32: keys per cluster (0 = empty);
+ *   order     [heads, tokens] int32: the keys sorted by (cluster, token), so
+ *             cluster j is order[h, off_j .. off_j + sizes[h, j]) with off_j
+ *             the sum of the sizes before j.
+ * The assignment runs on the matrix cores with 2 gram c_j split into two bf16
+ * terms (16 significant bits; fp64 products for fp32 keys); the sort is a
+ * stable counting sort and the means are fp64 sums rounded once, so results
+ * are deterministic.  ws / ws_bytes: at least rsa_workspace_bytes(p,
+ * RSA_OP_KMEANS) bytes, 256-byte aligned.
+ */
+rsa_status rsa_kmeans(const rsa_problem* p, const void* k, const float* gram, int32_t iters, int32_t init,
+                      float* centroids, int32_t* labels, int32_t* sizes, int32_t* order, void* ws,
+                      size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"rsa_workspace_bytes", "rsa_status_str", "rsa_version", "rsa_score_blocks",
                           "rsa_select_topp", "rsa_mask_drift", "rsa_block_sparse_attn",
                           "rsa_dense_block_mass", "rsa_score_blocks_pooled", "rsa_attn_omitted",
-                          "rsa_attn_merge"}
+                          "rsa_attn_merge", "rsa_query_gram", "rsa_kmeans"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -69,6 +69,14 @@ def test_workspace_sizes():
     lists = al(4 * 40 * 591) + al(4 * 40 * 591 * 591)
     assert B.workspace_bytes(p, B.OP_ATTN) == al(2 * 40 * 128 * 591 * 128) + lists
     assert B.workspace_bytes(prob(heads=40, grid=(21, 45, 80), b=128, dtype=1), B.OP_ATTN) == lists
+    # Gram matrix: one D x D fp32 partial per 2048 tokens (bf16 only)
+    assert B.workspace_bytes(p, B.OP_GRAM) == al(4 * 40 * 37 * 128 * 128)
+    assert B.workspace_bytes(prob(heads=40, grid=(21, 45, 80), b=128, dtype=1), B.OP_GRAM) == 0
+    # k-means: 2 G c split (2 x bf16) and fp32, b, block maxima, chunk histograms, ranks, offsets
+    nch = -(-75600 // 256)
+    assert B.workspace_bytes(p, B.OP_KMEANS) == (2 * al(2 * 40 * nbp * 128) + al(4 * 40 * nbp * 128)
+                                                 + al(4 * 40 * nbp) + al(4 * 40 * 591) + al(4 * 40 * nch * 591)
+                                                 + al(4 * 40 * 75600) + al(4 * 40 * 591))
     # query-pooled scorer: pooled q and k, then block maxima
     assert B.workspace_bytes(p, B.OP_POOLED) == 2 * al(4 * 40 * 591 * 128) + al(4 * 40 * 591)
     assert B.workspace_bytes(prob(d=96), B.OP_SCORE) == 0          # invalid problem -> 0
@@ -118,6 +126,9 @@ def test_null_problem_and_pointers(lib):
                                 b.ptr, 1 << 30, None) == NULL
     assert lib.rsa_attn_merge(ctypes.byref(p), b.ptr, b.ptr, b.ptr, None, None) == NULL
     assert lib.rsa_attn_merge(None, b.ptr, b.ptr, b.ptr, b.ptr, None) == NULL
+    assert lib.rsa_query_gram(ctypes.byref(p), None, b.ptr, b.ptr, 1 << 30, None) == NULL
+    assert lib.rsa_kmeans(ctypes.byref(p), b.ptr, b.ptr, 3, 1, b.ptr, b.ptr, None, b.ptr, b.ptr, 1 << 30,
+                          None) == NULL
     assert b.untouched()
 
 
@@ -165,6 +176,9 @@ def test_scalar_arguments(lib):
                               b.ptr, b.ptr, 1 << 30, None) == ARG
     assert lib.rsa_select_topp(ctypes.byref(p), b.ptr, b.ptr, -1, None, b.ptr, b.ptr, b.ptr, None,
                                None, 0, None) == ARG
+    for iters in (0, -2, 1001):                             # k-means runs 1..1000 iterations
+        assert lib.rsa_kmeans(ctypes.byref(p), b.ptr, b.ptr, iters, 1, b.ptr, b.ptr, b.ptr, b.ptr, b.ptr,
+                              1 << 30, None) == ARG
     assert b.untouched()
 
 

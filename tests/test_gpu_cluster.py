@@ -1,0 +1,152 @@
+"""PARK's query-aware key clustering on the GPU against the oracle.
+
+PARK (Accurate Block Retrieval for Sparse Attention in Video Diffusion
+Transformers), Abstract: keys are clustered in a metric built from the
+current queries, and the clusters serve as key blocks.
+
+* rsa_query_gram against the oracle's Gram matrix;
+* one Lloyd iteration at a time (rsa_kmeans with iters=1), the oracle given
+  the GPU's own starting centroids and Gram matrix: labels equal the oracle's
+  nearest centroids except where two centroids are within the assignment's
+  stated tolerance (reported); sizes and order are exact for the GPU's labels;
+  centroids equal the oracle's means of the GPU's clusters to one fp32
+  rounding;
+* several iterations in one call equal the same iterations one call at a
+  time, bit for bit, and repeat bit for bit;
+* keys that are all equal: every key ties, all go to cluster 0.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+import workloads as W
+import block_sparse_attention_scoring_amd as R
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda:0"
+
+CASES = {
+    # name: (heads, grid, head_dim, block, dtype)
+    "bf16_d128_b128": (2, (6, 20, 83), 128, 128, "bf16"),  # N=9960: 5 Gram chunks, NB=78
+    "bf16_d128_b64": (2, (3, 10, 41), 128, 64, "bf16"),    # N=1230, NB=20, last block 14
+    "bf16_d64_b64": (3, (4, 9, 37), 64, 64, "bf16"),       # N=1332, NB=21
+    "fp32_d64_b64": (1, (4, 8, 8), 64, 64, "fp32"),        # the tiny shape
+}
+# assignment: the GPU's 2 G c_j carries 16 significant bits; a choice that
+# differs from the oracle's must be within this share of k^T G k + c^T G c
+ASSIGN_TOL = 1e-4
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def host(t):
+    return t.detach().cpu().numpy()
+
+
+def workload(name):
+    h, grid, d, b, dt = CASES[name]
+    return W.Workload(300 + sorted(CASES).index(name), name, h, grid, d, b, dt, (0.9,))
+
+
+class Case:
+    def __init__(self, name):
+        wl = workload(name)
+        self.wl = wl
+        inp = W.make_inputs(wl)
+        say(f"[gpu] cluster case {name}: heads={wl.heads} tokens={wl.tokens} D={wl.head_dim} "
+            f"B={wl.block} NB={wl.nblocks} dtype={wl.dtype}")
+        self.q64, self.k64 = W.to_f64(inp.q), W.to_f64(inp.k)
+        self.q, self.k = inp.q.to(DEV).contiguous(), inp.k.to(DEV).contiguous()
+        self.p = R.make_problem(self.q, wl.grid, wl.block)
+        self.gram = R.query_gram(self.q, self.p)
+        torch.cuda.synchronize()
+
+
+_cases = {}
+
+
+def case(name):
+    if name not in _cases:
+        _cases[name] = Case(name)
+    return _cases[name]
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_gram_matches_oracle(name):
+    c = case(name)
+    g = host(c.gram).astype(np.float64)
+    for h in range(c.wl.heads):
+        want = O.query_gram(c.q64[h])
+        err = np.abs(g[h] - want).max() / np.abs(want).max()
+        say(f"[gpu] gram {name} h={h}: max rel err {err:.2e}")
+        assert err <= 1e-5 if c.wl.dtype == "bf16" else err <= 1e-7
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_kmeans_iterations_match_oracle(name):
+    c = case(name)
+    wl, p = c.wl, c.p
+    g = host(c.gram).astype(np.float64)
+    cent = None
+    near_ties = 0
+    for it in range(3):
+        prev = None if cent is None else cent.clone()
+        cent, labels, sizes, order = R.kmeans(c.k, c.gram, p, iters=1, init=it == 0,
+                                              centroids=None if it == 0 else prev.clone())
+        torch.cuda.synchronize()
+        lab, sz, od, cg = host(labels), host(sizes), host(order), host(cent).astype(np.float64)
+        for h in range(wl.heads):
+            start = O.pool_keys(c.k64[h], wl.block).astype(np.float32).astype(np.float64) if prev is None \
+                else host(prev[h]).astype(np.float64)
+            want, dist = O.assign(c.k64[h], start, g[h])
+            diff = np.flatnonzero(lab[h] != want)
+            if diff.size:
+                kgk = ((c.k64[h][diff] @ g[h]) * c.k64[h][diff]).sum(1)
+                cgc = ((start[lab[h][diff]] @ g[h]) * start[lab[h][diff]]).sum(1)
+                gap = dist[diff, lab[h][diff]] - dist[diff, want[diff]]
+                assert (gap <= ASSIGN_TOL * (kgk + cgc)).all(), (it, h, diff[:5], gap[:5])
+                near_ties += diff.size
+            assert (sz[h] == np.bincount(lab[h], minlength=wl.nblocks)).all()
+            assert (od[h] == O.cluster_order(lab[h])).all()
+            c_or, _ = O.update(c.k64[h], lab[h], start)
+            np.testing.assert_allclose(cg[h], c_or, rtol=2 ** -23, atol=1e-30)
+        say(f"[gpu] kmeans {name} iteration {it}: non-empty clusters "
+            f"{[(int((sz[h] > 0).sum())) for h in range(wl.heads)]}, near-tie labels so far {near_ties}")
+    assert near_ties <= max(1, wl.tokens * wl.heads // 1000)
+
+
+def test_kmeans_several_iterations_in_one_call():
+    c = case("bf16_d64_b64")
+    out4 = R.kmeans(c.k, c.gram, c.p, iters=4)
+    again = R.kmeans(c.k, c.gram, c.p, iters=4)
+    cent = R.kmeans(c.k, c.gram, c.p, iters=1)[0]
+    for _ in range(3):
+        step = R.kmeans(c.k, c.gram, c.p, iters=1, init=False, centroids=cent)
+        cent = step[0]
+    torch.cuda.synchronize()
+    for a, b_, s in zip(out4, again, step):
+        assert torch.equal(a, b_) and torch.equal(a, s)
+
+
+def test_kmeans_all_keys_equal():
+    """Every key the same: all block means equal, every key ties with every
+    cluster and goes to cluster 0; the other clusters stay empty."""
+    wl = W.Workload(330, "equal_keys", 2, (2, 8, 25), 128, 64, "bf16", (0.9,))   # N=400, NB=7
+    inp = W.make_inputs(wl)
+    q = inp.q.to(DEV)
+    k = inp.k[:, :1, :].expand(-1, wl.tokens, -1).contiguous().to(DEV)
+    p = R.make_problem(q, wl.grid, wl.block)
+    gram = R.query_gram(q, p)
+    cent, labels, sizes, order = R.kmeans(k, gram, p, iters=2)
+    torch.cuda.synchronize()
+    assert (labels == 0).all()
+    assert host(sizes).tolist() == [[wl.tokens] + [0] * (wl.nblocks - 1)] * wl.heads
+    assert (host(order) == np.arange(wl.tokens)[None, :]).all()
+    want = inp.k[:, 0, :].float()
+    assert torch.equal(cent.cpu(), want[:, None, :].expand(-1, wl.nblocks, -1))
