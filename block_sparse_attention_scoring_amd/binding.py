@@ -19,7 +19,7 @@ LIB_PATH = os.path.join(_PKG, "lib", "librsa.so")
 HEADER = os.path.join(os.path.dirname(_PKG), "include", "rsa.h")
 
 RSA_BF16, RSA_FP32 = 0, 1
-OP_SCORE, OP_SELECT, OP_DRIFT, OP_ATTN, OP_POOLED, OP_GRAM, OP_KMEANS = 0, 1, 2, 3, 4, 5, 6
+OP_SCORE, OP_SELECT, OP_DRIFT, OP_ATTN, OP_POOLED, OP_GRAM, OP_KMEANS, OP_CLUSTER_ATTN = range(8)
 
 
 class RsaLibraryMissing(RuntimeError):
@@ -77,6 +77,8 @@ def _declare(lib):
         "rsa_attn_merge": (i32, [pp, _P, _P, _P, _P, _P]),
         "rsa_query_gram": (i32, [pp, _P, _P, _P, sz, _P]),
         "rsa_kmeans": (i32, [pp, _P, _P, i32, i32, _P, _P, _P, _P, _P, sz, _P]),
+        "rsa_score_clusters": (i32, [pp, _P, _P, _P, _P, _P, sz, _P]),
+        "rsa_cluster_attn": (i32, [pp, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -274,3 +276,28 @@ def kmeans(k, gram, p: Problem, iters: int, init: bool = True, centroids=None, l
     _check(lib().rsa_kmeans(ctypes.byref(p), _ptr(k), _ptr(gram), int(iters), int(bool(init)), _ptr(centroids),
                             _ptr(labels), _ptr(sizes), _ptr(order), _ptr(ws), wsb, _stream(k)), "rsa_kmeans")
     return centroids, labels, sizes, order
+
+
+def score_clusters(q, centroids, sizes, p: Problem, out=None, workspace=None):
+    """PARK scores with clusters as key blocks, [heads, NB, NB] fp32 (rsa_score_clusters)."""
+    nb = p.nblocks
+    if out is None:
+        out = torch.empty((p.heads, nb, nb), dtype=torch.float32, device=q.device)
+    ws, wsb = _workspace(p, OP_SCORE, q.device, workspace)
+    _check(lib().rsa_score_clusters(ctypes.byref(p), _ptr(q), _ptr(centroids), _ptr(sizes), _ptr(out), _ptr(ws),
+                                    wsb, _stream(q)), "rsa_score_clusters")
+    return out
+
+
+def cluster_attn(q, k, v, sizes, order, counts, block_idx, p: Problem, out=None, lse=None, want_lse: bool = True,
+                 workspace=None):
+    """Attention over the listed clusters' keys -> (out like q, lse fp32 [H, N] or None) (rsa_cluster_attn)."""
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((p.heads, p.tokens), dtype=torch.float32, device=q.device)
+    ws, wsb = _workspace(p, OP_CLUSTER_ATTN, q.device, workspace)
+    _check(lib().rsa_cluster_attn(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(sizes), _ptr(order),
+                                  _ptr(counts), _ptr(block_idx), _ptr(out), _ptr(lse), _ptr(ws), wsb, _stream(q)),
+           "rsa_cluster_attn")
+    return out, lse

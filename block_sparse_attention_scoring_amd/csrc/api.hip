@@ -48,6 +48,7 @@ size_t ws_bytes_for(const rsa::Problem& p, int op) {
     case RSA_OP_POOLED: return rsa::pooled_ws_bytes(p);
     case RSA_OP_GRAM: return rsa::gram_ws_bytes(p);
     case RSA_OP_KMEANS: return rsa::kmeans_ws_bytes(p);
+    case RSA_OP_CLUSTER_ATTN: return rsa::cluster_attn_ws_bytes(p);
     default: return 0;
   }
 }
@@ -227,6 +228,36 @@ rsa_status rsa_kmeans(const rsa_problem* p, const void* k, const float* gram, in
   st = check_ws(pr, RSA_OP_KMEANS, ws, ws_bytes);
   if (st != RSA_OK) return st;
   return hip_status(rsa::launch_kmeans(pr, k, gram, iters, init != 0, centroids, labels, sizes, order, ws, stream));
+}
+
+rsa_status rsa_score_clusters(const rsa_problem* p, const void* q, const float* centroids, const int32_t* sizes,
+                              float* scores, void* ws, size_t ws_bytes, hipStream_t stream) {
+  rsa::Problem pr;
+  rsa_status st = make_problem(p, &pr);
+  if (st != RSA_OK) return st;
+  if (q == nullptr || centroids == nullptr || sizes == nullptr || scores == nullptr) return RSA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(scores)) return RSA_ERR_ALIGN;
+  st = check_ws(pr, RSA_OP_SCORE, ws, ws_bytes);
+  if (st != RSA_OK) return st;
+  rsa::ScoreWs w;
+  rsa::score_ws_layout(pr, &w, ws);
+  return hip_status(rsa::launch_cluster_scoring(pr, q, centroids, sizes, scores, w, stream));
+}
+
+rsa_status rsa_cluster_attn(const rsa_problem* p, const void* q, const void* k, const void* v, const int32_t* sizes,
+                            const int32_t* order, const int32_t* counts, const int32_t* block_idx, void* out,
+                            float* lse, void* ws, size_t ws_bytes, hipStream_t stream) {
+  rsa::Problem pr;
+  rsa_status st = make_problem(p, &pr);
+  if (st != RSA_OK) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || sizes == nullptr || order == nullptr || counts == nullptr ||
+      block_idx == nullptr || out == nullptr)
+    return RSA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return RSA_ERR_ALIGN;
+  st = check_ws(pr, RSA_OP_CLUSTER_ATTN, ws, ws_bytes);
+  if (st != RSA_OK) return st;
+  return hip_status(
+      rsa::launch_cluster_attention(pr, q, k, v, sizes, order, counts, block_idx, out, lse, ws, stream));
 }
 
 }  // extern "C"

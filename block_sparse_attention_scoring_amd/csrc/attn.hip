@@ -156,14 +156,21 @@ __global__ __launch_bounds__(256) void vt_kernel(const uint16_t* __restrict__ v,
 // matrix products for sub-tile j run next to the exponentials of sub-tile
 // j-1.  Two workgroups share a CU, so the two waves on every SIMD also
 // overlap each other's vector and matrix work.
-template <int D, int B, int KS, int NBUF>
+//
+// kTable: the row lists 32-key sub-tiles instead of key blocks (clusters as
+// key blocks): entry e is a sub-tile at key e & ~31 of the padded cluster
+// layout holding (e & 31) + 1 real keys; K has Nk rows and V^T Nv columns per
+// head.  Every sub-tile may be partial, so each step applies its mask.
+template <int D, int B, int KS, int NBUF, bool kTable = false>
 __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const int* __restrict__ ccount,
     const int* __restrict__ clist, const uint8_t* __restrict__ head_active,
-    uint16_t* __restrict__ out, float* __restrict__ lse, int H, int N, int NB, float scale_log2) {
+    uint16_t* __restrict__ out, float* __restrict__ lse, int H, int N, int NB, float scale_log2,
+    int Nk, int Nv, int lstride) {
   using S = AttnShape<D, B, KS, NBUF>;
   static_assert(NBUF >= 3 && NBUF <= 4, "ring of 3 or 4 LDS slots");
+  static_assert(!kTable || KS == 32, "table entries are 32-key sub-tiles");
   // Ring slots: K sub-tile at [0, kTile), V^T sub-tile after it.  Separate
   // arrays, addressed with compile-time slot numbers, let the compiler see
   // that the slot being filled is not the one being read, so it does not
@@ -186,7 +193,7 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS addresses stay scalar
   const int hl = lane >> 5, col = lane & 31;
   const size_t head_off = static_cast<size_t>(h) * N * D;
-  const size_t np = static_cast<size_t>(NB) * B;
+  const size_t np = static_cast<size_t>(Nv);
   const int qrow = I * B + wave * 32 + col;
 
   bf16x8 qf[S::kKSD];
@@ -201,13 +208,16 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
   }
 
   const int cnt = ccount[h * NB + I];
-  const int total = cnt * S::kSub;  // sub-tiles to visit
-  const int* list = clist + (static_cast<size_t>(h) * NB + I) * NB;
-  const uint16_t* kh = k + head_off;
+  const int total = kTable ? cnt : cnt * S::kSub;  // sub-tiles to visit
+  const int* list = clist + (static_cast<size_t>(h) * NB + I) * lstride;
+  const uint16_t* kh = k + static_cast<size_t>(h) * Nk * D;
   const uint16_t* vth = vt + static_cast<size_t>(h) * D * np;
 
-  // first key and number of real keys of sub-tile u
-  auto sub_base = [&](int u) { return list[u / S::kSub] * B + (u % S::kSub) * KS; };
+  // first key of sub-tile u
+  auto sub_base = [&](int u) {
+    if constexpr (kTable) return list[u] & ~31;
+    else return list[u / S::kSub] * B + (u % S::kSub) * KS;
+  };
 
   // Tiles are fetched with buffer loads straight into LDS.  Each lane's byte
   // offset inside a sub-tile is fixed for the whole loop, so only scalar
@@ -230,7 +240,7 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
   auto issue = [&](int u, uint16_t* dst) {
     const int kbase = sub_base(u);
     const __amdgpu_buffer_rsrc_t krsrc = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(kh + static_cast<size_t>(kbase) * D), 0, max(N - kbase, 0) * D * 2, kRsrcWord3);
+        const_cast<uint16_t*>(kh + static_cast<size_t>(kbase) * D), 0, max(Nk - kbase, 0) * D * 2, kRsrcWord3);
 #pragma unroll
     for (int i = 0; i < S::kLoads; ++i) {
       const int blk = wave * S::kLoads + i;  // 1 KB block of the sub-tile
@@ -281,9 +291,10 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
       for (int t = 0; t < S::kKT; ++t) sacc[t] = mfma32(a[t], qf[s], sacc[t]);
     }
   };
-  // keys at or past the last token (tail sub-tile only) get score -inf
+  // keys at or past the last token (tail sub-tile only) get score -inf; in
+  // table mode the keys past the sub-tile's count
   auto mask_tail = [&](int u, f32x16* sacc) {
-    const int valid = N - sub_base(u);
+    const int valid = kTable ? (list[u] & 31) + 1 : N - sub_base(u);
     if (valid < KS) {
 #pragma unroll
       for (int t = 0; t < S::kKT; ++t)
@@ -359,7 +370,7 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
   // leading sub-tiles with no key past the last token: the canonical list is
   // ascending, so only its last entry can be the ragged block NB-1
   int total_full = total;
-  if (total > 0) {
+  if (!kTable && total > 0) {
     const int last = list[cnt - 1];
     if (last == NB - 1) total_full = total - S::kSub + min(S::kSub, (N - last * B) / KS);
   }
@@ -372,6 +383,7 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
     barrier_lds();
     issue(NBUF - 2, ring(NBUF - 2));
     qk(slot0, sprev);
+    if constexpr (kTable) mask_tail(0, sprev);
     mprev = rowmax(sprev);
     j = 1;
     pending = true;
@@ -385,6 +397,7 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
       pv(sprev, vslot);
 #pragma unroll
       for (int t = 0; t < S::kKT; ++t) sprev[t] = scur[t];
+      if constexpr (kTable) mask_tail(jj, sprev);
       mprev = rowmax(sprev);
     };
     // groups of NBUF steps starting at j = 1 mod NBUF: compile-time slots
@@ -436,12 +449,14 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
 // fp32 inputs: plain fp32 arithmetic, one thread per query row, K and V
 // staged in LDS 32 keys at a time and read as broadcasts, over the canonical
 // list.  Same online softmax (exact rescaling at every chunk).
-template <int D, int B>
+// kTable: as in attn_bf16_kernel; k and v are the padded cluster layout,
+// row-major, Nk rows per head.
+template <int D, int B, bool kTable = false>
 __global__ __launch_bounds__(B) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int* __restrict__ ccount, const int* __restrict__ clist,
     const uint8_t* __restrict__ head_active, float* __restrict__ out, float* __restrict__ lse,
-    int N, int NB, float scale_log2) {
+    int N, int NB, float scale_log2, int Nk, int lstride) {
   constexpr int kChunk = 32;
   __shared__ float Ks[kChunk * D];
   __shared__ float Vs[kChunk * D];
@@ -459,16 +474,17 @@ __global__ __launch_bounds__(B) void attn_f32_kernel(
   }
   float m = -INFINITY, l = 0.f;
   const int cnt = ccount[h * NB + I];
-  const int* list = clist + (static_cast<size_t>(h) * NB + I) * NB;
+  const int* list = clist + (static_cast<size_t>(h) * NB + I) * lstride;
+  const size_t kv_off = static_cast<size_t>(h) * Nk * D;
   for (int it = 0; it < cnt; ++it) {
-    const int kbase = list[it] * B;
-    const int bJ = min(B, N - kbase);
+    const int kbase = kTable ? list[it] & ~31 : list[it] * B;
+    const int bJ = kTable ? (list[it] & 31) + 1 : min(B, N - kbase);
     for (int kc = 0; kc < bJ; kc += kChunk) {
       const int nk = min(kChunk, bJ - kc);
       __syncthreads();
       for (int e = tid; e < kChunk * D; e += B) {
         const int row = e / D;
-        const size_t g = head_off + static_cast<size_t>(kbase + kc) * D + e;
+        const size_t g = kv_off + static_cast<size_t>(kbase + kc) * D + e;
         Ks[e] = row < nk ? k[g] : 0.f;
         Vs[e] = row < nk ? v[g] : 0.f;
       }
@@ -550,16 +566,276 @@ hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const v
     const int grid = 8 * ((p.nb + 7) / 8) * p.heads;
     hipLaunchKernelGGL((attn_bf16_kernel<D, B, kKs, kNbuf>), dim3(grid), dim3(S::kThreads), 0, stream,
                        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt, ccount,
-                       clist, head_active, static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2);
+                       clist, head_active, static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2,
+                       p.tokens, p.nb * B, p.nb);
   } else {
     hipLaunchKernelGGL((attn_f32_kernel<D, B>), dim3(p.heads * p.nb), dim3(B), 0, stream,
                        static_cast<const float*>(q), static_cast<const float*>(k),
                        static_cast<const float*>(v), ccount, clist, head_active,
-                       static_cast<float*>(out), lse, p.tokens, p.nb, sl2);
+                       static_cast<float*>(out), lse, p.tokens, p.nb, sl2, p.tokens, p.nb);
   }
   return hipGetLastError();
 }
 
+
+// ------------------------------------------------------------ clusters as key blocks
+// Keys of cluster j sit at [pstart_j, pstart_j + 32 * ceil(size_j / 32)) of a
+// padded per-head layout, in the order rsa_kmeans sorted them (order), with
+// zero keys and values in the padding; every 32-key sub-tile of the layout
+// lies inside one cluster.
+
+// Per head: pstart (exclusive sum of the padded sizes) and ostart (exclusive
+// sum of the sizes: where the cluster starts in `order`).
+__global__ __launch_bounds__(256) void cl_scan_kernel(const int* __restrict__ sizes, int* __restrict__ pstart,
+                                                      int* __restrict__ ostart, int NB) {
+  constexpr int kPer = kMaxNB / 256;
+  __shared__ int2 part[256];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  const int* sz = sizes + static_cast<size_t>(h) * NB;
+  int2 local = make_int2(0, 0);
+  for (int e = 0; e < kPer; ++e) {
+    const int j = tid * kPer + e;
+    if (j < NB) {
+      const int n = max(sz[j], 0);
+      local.x += (n + 31) & ~31;
+      local.y += n;
+    }
+  }
+  part[tid] = local;
+  __syncthreads();
+  if (tid == 0) {
+    int2 run = make_int2(0, 0);
+    for (int i = 0; i < 256; ++i) {
+      const int2 v = part[i];
+      part[i] = run;
+      run.x += v.x;
+      run.y += v.y;
+    }
+  }
+  __syncthreads();
+  int2 run = part[tid];
+  for (int e = 0; e < kPer; ++e) {
+    const int j = tid * kPer + e;
+    if (j < NB) {
+      pstart[static_cast<size_t>(h) * NB + j] = run.x;
+      ostart[static_cast<size_t>(h) * NB + j] = run.y;
+      const int n = max(sz[j], 0);
+      run.x += (n + 31) & ~31;
+      run.y += n;
+    }
+  }
+}
+
+// One workgroup per (cluster, head): K rows into the padded layout and V^T
+// columns (vt_pos order inside every 16 keys, as the attention kernel reads
+// them), 32 keys at a time through an LDS tile.
+template <int D>
+__global__ __launch_bounds__(256) void cl_gather_bf16_kernel(const uint16_t* __restrict__ k,
+                                                             const uint16_t* __restrict__ v,
+                                                             const int* __restrict__ sizes,
+                                                             const int* __restrict__ order,
+                                                             const int* __restrict__ pstart,
+                                                             const int* __restrict__ ostart,
+                                                             uint16_t* __restrict__ kp, uint16_t* __restrict__ vtp,
+                                                             int N, int NB, int Np) {
+  __shared__ uint16_t tile[32][D + 2];
+  const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const size_t row = static_cast<size_t>(h) * NB + j;
+  const int n = sizes[row];
+  if (n <= 0) return;
+  const int ps = pstart[row];
+  const int* ord = order + static_cast<size_t>(h) * N + ostart[row];
+  for (int s0 = 0; s0 < n; s0 += 32) {
+    __syncthreads();
+    for (int c = tid; c < 32 * D / 8; c += 256) {
+      const int r = c / (D / 8), c8 = c % (D / 8);
+      const int tok = s0 + r < n ? ord[s0 + r] : -1;
+      u32x4 kx = u32x4{0, 0, 0, 0}, vx = u32x4{0, 0, 0, 0};
+      if (tok >= 0) {
+        const size_t g = (static_cast<size_t>(h) * N + tok) * D + c8 * 8;
+        kx = *reinterpret_cast<const u32x4*>(k + g);
+        vx = *reinterpret_cast<const u32x4*>(v + g);
+      }
+      *reinterpret_cast<u32x4*>(kp + (static_cast<size_t>(h) * Np + ps + s0 + r) * D + c8 * 8) = kx;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        tile[r][c8 * 8 + 2 * e] = static_cast<uint16_t>(vx[e] & 0xffffu);
+        tile[r][c8 * 8 + 2 * e + 1] = static_cast<uint16_t>(vx[e] >> 16);
+      }
+    }
+    __syncthreads();
+    for (int c = tid; c < D * 4; c += 256) {
+      const int d = c / 4, p8 = c % 4;
+      u32x4 o;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = tile[vt_pos(8 * p8 + 2 * e)][d];
+        const uint32_t hi = tile[vt_pos(8 * p8 + 2 * e + 1)][d];
+        o[e] = lo | (hi << 16);
+      }
+      *reinterpret_cast<u32x4*>(vtp + (static_cast<size_t>(h) * D + d) * Np + ps + s0 + 8 * p8) = o;
+    }
+  }
+}
+
+// fp32: K and V rows into the padded layout, row-major.
+template <int D>
+__global__ __launch_bounds__(256) void cl_gather_f32_kernel(const float* __restrict__ k, const float* __restrict__ v,
+                                                            const int* __restrict__ sizes,
+                                                            const int* __restrict__ order,
+                                                            const int* __restrict__ pstart,
+                                                            const int* __restrict__ ostart, float* __restrict__ kp,
+                                                            float* __restrict__ vp, int N, int NB, int Np) {
+  const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const size_t row = static_cast<size_t>(h) * NB + j;
+  const int n = sizes[row];
+  if (n <= 0) return;
+  const int ps = pstart[row], npad = (n + 31) & ~31;
+  const int* ord = order + static_cast<size_t>(h) * N + ostart[row];
+  for (int c = tid; c < npad * D / 4; c += 256) {
+    const int r = c / (D / 4), c4 = (c % (D / 4)) * 4;
+    const int tok = r < n ? ord[r] : -1;
+    f32x4 kx = f32x4{0.f, 0.f, 0.f, 0.f}, vx = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (tok >= 0) {
+      const size_t g = (static_cast<size_t>(h) * N + tok) * D + c4;
+      kx = *reinterpret_cast<const f32x4*>(k + g);
+      vx = *reinterpret_cast<const f32x4*>(v + g);
+    }
+    const size_t o = (static_cast<size_t>(h) * Np + ps + r) * D + c4;
+    *reinterpret_cast<f32x4*>(kp + o) = kx;
+    *reinterpret_cast<f32x4*>(vp + o) = vx;
+  }
+}
+
+// Inclusive prefix sum over the 256 threads of a workgroup (wave scans, then
+// the four wave totals); `wsum` is LDS scratch of 4 ints.
+__device__ __forceinline__ int block_scan_256(int x, int* wsum, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == 63) wsum[wave] = x;
+  __syncthreads();
+  int before = 0, all = 0;
+#pragma unroll
+  for (int w = 0; w < 4; ++w) {
+    before += w < wave ? wsum[w] : 0;
+    all += wsum[w];
+  }
+  __syncthreads();
+  *total = all;
+  return x + before;
+}
+
+// Sub-tile table of one row (query block I, head h): the row's listed
+// clusters as a set (as canon_kernel reads lists), ascending, empty ones
+// dropped; cluster j contributes ceil(size_j / 32) entries
+// pstart_j + 32 s + (real keys of sub-tile s) - 1.
+__global__ __launch_bounds__(256) void cl_table_kernel(const int* __restrict__ counts,
+                                                       const int* __restrict__ block_idx,
+                                                       const int* __restrict__ sizes,
+                                                       const int* __restrict__ pstart, int* __restrict__ tcount,
+                                                       int* __restrict__ table, int NB, int stride) {
+  __shared__ uint8_t mark[kMaxNB];
+  __shared__ int wsum[4];
+  const int I = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const size_t row = static_cast<size_t>(h) * NB + I;
+  for (int e = tid; e < NB; e += 256) mark[e] = 0;
+  __syncthreads();
+  const int c = min(max(counts[row], 0), NB);
+  for (int t = tid; t < c; t += 256) {
+    const int j = block_idx[row * NB + t];
+    if (static_cast<unsigned>(j) < static_cast<unsigned>(NB)) mark[j] = 1;
+  }
+  __syncthreads();
+  int* out = table + row * stride;
+  int base = 0;
+  for (int r0 = 0; r0 < NB; r0 += 256) {
+    const int j = r0 + tid;
+    const int n = j < NB && mark[j] ? sizes[static_cast<size_t>(h) * NB + j] : 0;
+    const int w = n > 0 ? (n + 31) >> 5 : 0;
+    int tot;
+    const int incl = block_scan_256(w, wsum, &tot);
+    if (w > 0) {
+      const int ps = pstart[static_cast<size_t>(h) * NB + j];
+      int* dst = out + base + incl - w;
+      for (int s = 0; s < w; ++s) dst[s] = ps + 32 * s + (min(32, n - 32 * s) - 1);
+    }
+    base += tot;
+  }
+  if (tid == 0) tcount[row] = base;
+}
+
+struct ClAttnWs {
+  size_t kp_off, vp_off, pstart_off, ostart_off, tcount_off, table_off, total;
+  int Np, stride;
+};
+
+ClAttnWs cl_attn_ws_layout(const Problem& p) {
+  auto al = [](size_t x) { return (x + 255) / 256 * 256; };
+  ClAttnWs w;
+  // every cluster padded to whole 32-key sub-tiles: at most 31 * NB extra keys
+  w.Np = (p.tokens + 31 * p.nb + 31) / 32 * 32;
+  w.stride = w.Np / 32;  // sub-tiles per row at most
+  const size_t es = p.dtype == 0 ? 2 : 4;
+  const size_t kv = al(es * p.heads * static_cast<size_t>(w.Np) * p.head_dim);
+  const size_t rows = static_cast<size_t>(p.heads) * p.nb;
+  w.kp_off = 0;
+  w.vp_off = kv;
+  w.pstart_off = 2 * kv;
+  w.ostart_off = w.pstart_off + al(4 * rows);
+  w.tcount_off = w.ostart_off + al(4 * rows);
+  w.table_off = w.tcount_off + al(4 * rows);
+  w.total = w.table_off + al(4 * rows * w.stride);
+  return w;
+}
+
+template <int D, int B>
+hipError_t launch_cluster_attn_t(const Problem& p, const void* q, const void* k, const void* v, const int* sizes,
+                                 const int* order, const int* counts, const int* idx, void* out, float* lse,
+                                 void* ws, hipStream_t stream) {
+  const float sl2 = p.scale * kLog2e;
+  const ClAttnWs w = cl_attn_ws_layout(p);
+  char* base = static_cast<char*>(ws);
+  int* pstart = reinterpret_cast<int*>(base + w.pstart_off);
+  int* ostart = reinterpret_cast<int*>(base + w.ostart_off);
+  int* tcount = reinterpret_cast<int*>(base + w.tcount_off);
+  int* table = reinterpret_cast<int*>(base + w.table_off);
+  hipLaunchKernelGGL(cl_scan_kernel, dim3(p.heads), dim3(256), 0, stream, sizes, pstart, ostart, p.nb);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (p.dtype == 0)
+    hipLaunchKernelGGL((cl_gather_bf16_kernel<D>), dim3(p.nb, p.heads), dim3(256), 0, stream,
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), sizes, order, pstart,
+                       ostart, reinterpret_cast<uint16_t*>(base + w.kp_off),
+                       reinterpret_cast<uint16_t*>(base + w.vp_off), p.tokens, p.nb, w.Np);
+  else
+    hipLaunchKernelGGL((cl_gather_f32_kernel<D>), dim3(p.nb, p.heads), dim3(256), 0, stream,
+                       static_cast<const float*>(k), static_cast<const float*>(v), sizes, order, pstart, ostart,
+                       reinterpret_cast<float*>(base + w.kp_off), reinterpret_cast<float*>(base + w.vp_off),
+                       p.tokens, p.nb, w.Np);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipLaunchKernelGGL(cl_table_kernel, dim3(p.nb, p.heads), dim3(256), 0, stream, counts, idx, sizes, pstart,
+                     tcount, table, p.nb, w.stride);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if (p.dtype == 0) {
+    constexpr int kNbuf = B == 128 ? RSA_ATTN_NBUF : 3;
+    using S = AttnShape<D, B, 32, kNbuf>;
+    const int grid = 8 * ((p.nb + 7) / 8) * p.heads;
+    hipLaunchKernelGGL((attn_bf16_kernel<D, B, 32, kNbuf, true>), dim3(grid), dim3(S::kThreads), 0, stream,
+                       static_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(base + w.kp_off),
+                       reinterpret_cast<const uint16_t*>(base + w.vp_off), tcount, table, nullptr,
+                       static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2, w.Np, w.Np, w.stride);
+  } else {
+    hipLaunchKernelGGL((attn_f32_kernel<D, B, true>), dim3(p.heads * p.nb), dim3(B), 0, stream,
+                       static_cast<const float*>(q), reinterpret_cast<const float*>(base + w.kp_off),
+                       reinterpret_cast<const float*>(base + w.vp_off), tcount, table, nullptr,
+                       static_cast<float*>(out), lse, p.tokens, p.nb, sl2, w.Np, w.stride);
+  }
+  return hipGetLastError();
+}
 }  // namespace
 
 size_t attn_ws_bytes(const Problem& p) { return attn_ws_layout(p).total; }
@@ -572,6 +848,18 @@ hipError_t launch_attention(const Problem& p, const void* q, const void* k, cons
   if (p.head_dim == 128 && p.block == 64) return go(launch_attn_t<128, 64>);
   if (p.head_dim == 64 && p.block == 128) return go(launch_attn_t<64, 128>);
   return go(launch_attn_t<64, 64>);
+}
+
+size_t cluster_attn_ws_bytes(const Problem& p) { return cl_attn_ws_layout(p).total; }
+
+hipError_t launch_cluster_attention(const Problem& p, const void* q, const void* k, const void* v,
+                                    const int* sizes, const int* order, const int* counts, const int* idx,
+                                    void* out, float* lse, void* ws, hipStream_t stream) {
+  auto go = [&](auto fn) { return fn(p, q, k, v, sizes, order, counts, idx, out, lse, ws, stream); };
+  if (p.head_dim == 128 && p.block == 128) return go(launch_cluster_attn_t<128, 128>);
+  if (p.head_dim == 128 && p.block == 64) return go(launch_cluster_attn_t<128, 64>);
+  if (p.head_dim == 64 && p.block == 128) return go(launch_cluster_attn_t<64, 128>);
+  return go(launch_cluster_attn_t<64, 64>);
 }
 
 }  // namespace rsa

@@ -35,6 +35,10 @@ size_t drift_ws_bytes(const Problem& p);
 hipError_t launch_scoring(const Problem& p, const void* q, const void* k,
                           const uint8_t* head_active, float* scores, const ScoreWs& ws,
                           hipStream_t stream);
+// The same scores with clusters as key blocks: centroids [H, NB, D] fp32 as
+// the pooled keys, empty clusters (sizes 0) left out of every softmax.
+hipError_t launch_cluster_scoring(const Problem& p, const void* q, const float* cent, const int* sizes,
+                                  float* scores, const ScoreWs& ws, hipStream_t stream);
 hipError_t launch_select(const Problem& p, const float* scores, const float* top_p,
                          int max_blocks, const uint8_t* head_active, uint8_t* mask,
                          int32_t* counts, int32_t* idx, float* density, hipStream_t stream);
@@ -49,6 +53,13 @@ size_t attn_ws_bytes(const Problem& p);
 hipError_t launch_attention(const Problem& p, const void* q, const void* k, const void* v,
                             const int* counts, const int* idx, const uint8_t* head_active,
                             int complement, void* out, float* lse, void* ws, hipStream_t stream);
+// Attention with clusters as key blocks (lists name clusters): K and V are
+// gathered into a padded cluster layout, each row's clusters become a table
+// of 32-key sub-tiles, and the attention kernels walk the tables.
+size_t cluster_attn_ws_bytes(const Problem& p);
+hipError_t launch_cluster_attention(const Problem& p, const void* q, const void* k, const void* v,
+                                    const int* sizes, const int* order, const int* counts, const int* idx,
+                                    void* out, float* lse, void* ws, hipStream_t stream);
 // In place: (out, lse) <- attention over the union of the key sets behind
 // (out, lse) and (part, part_lse), two disjoint parts.
 hipError_t launch_merge(const Problem& p, void* out, float* lse, const void* part,

@@ -205,11 +205,13 @@ __device__ __forceinline__ void lds_store_f32(float* p, float v) {
   asm volatile("ds_write_b32 %0, %1" ::"v"(a), "v"(v) : "memory");
 }
 
-template <typename T, int D, int B, int NBUF>
+// kColMask: key "blocks" are clusters, some possibly empty (colsize 0); an
+// empty cluster takes no part in any query's softmax and scores 0.
+template <typename T, int D, int B, int NBUF, bool kColMask = false>
 __global__ __launch_bounds__(2 * B, 2) void score_kernel(
     const T* __restrict__ q, const _Float16* __restrict__ khi, const _Float16* __restrict__ klo,
     const float* __restrict__ inv_t, const uint8_t* __restrict__ head_active,
-    float* __restrict__ scores, int N, int NB, int NBp) {
+    const int* __restrict__ colsize, float* __restrict__ scores, int N, int NB, int NBp) {
   constexpr bool kSplitQ = sizeof(T) == 4;
   constexpr int kWaves = B / 32, kThreads = kWaves * kWave;
   constexpr int kKS = D / 16;                              // k-steps over head_dim
@@ -324,6 +326,11 @@ __global__ __launch_bounds__(2 * B, 2) void score_kernel(
   float mraw = -INFINITY, z = 0.f;  // pass 1, this half's key blocks
   float qs[16], qm[16];              // pass 2: per register (query) constants
   float* srow = scores + (static_cast<size_t>(h) * NB + I) * NB;
+  // column 32c + col of this lane holds keys (cluster mode)
+  auto live_col = [&](int c) __attribute__((always_inline)) {
+    const int j = 32 * c + col;
+    return j < NB && colsize[static_cast<size_t>(h) * NB + j] > 0;
+  };
   // all waves' partial sums of chunk c are in part[c & 1]
   auto finish = [&](int c) __attribute__((always_inline)) {
     if (wave == 0 && lane < 32 && 32 * c + lane < NB) {
@@ -336,7 +343,13 @@ __global__ __launch_bounds__(2 * B, 2) void score_kernel(
   auto body = [&](int u, const _Float16* cur) __attribute__((always_inline)) {
     if (u < nc) {
       f32x16 acc = logits(u, cur, std::true_type{});
-      if (32 * u + 32 > NB) {
+      if constexpr (kColMask) {
+        // lane col's bit says whether column 32u + col is a live cluster
+        const uint32_t live = static_cast<uint32_t>(__ballot(live_col(u)));
+#pragma unroll
+        for (int r = 0; r < 16; ++r)
+          if (!((live >> acc_row(r, hl)) & 1u)) acc[r] = -INFINITY;
+      } else if (32 * u + 32 > NB) {
 #pragma unroll
         for (int r = 0; r < 16; ++r)
           if (32 * u + acc_row(r, hl) >= NB) acc[r] = -INFINITY;
@@ -387,6 +400,9 @@ __global__ __launch_bounds__(2 * B, 2) void score_kernel(
     for (int r = 0; r < 16; ++r) ps[r & 3] += __builtin_amdgcn_exp2f(fmaf(acc[r], qs[r], qm[r]));
     float t = (ps[0] + ps[1]) + (ps[2] + ps[3]);
     t += __shfl_xor(t, 32);  // the other 16 queries
+    if constexpr (kColMask) {
+      if (!live_col(c)) t = 0.f;
+    }
     if (hl == 0) lds_store_f32(&part[c & 1][wave][col], t);
   };
 
@@ -440,12 +456,56 @@ hipError_t launch_scoring_t(const Problem& p, const void* q, const void* k,
   const int grid = p.heads * p.nb;
   if (p.block == 128)
     hipLaunchKernelGGL((score_kernel<T, D, 128, 4>), dim3(grid), dim3(256), 0, stream,
-                       static_cast<const T*>(q), ws.khi, ws.klo, ws.inv_t, head_active, scores,
+                       static_cast<const T*>(q), ws.khi, ws.klo, ws.inv_t, head_active, nullptr, scores,
                        p.tokens, p.nb, NBp);
   else
     hipLaunchKernelGGL((score_kernel<T, D, 64, 4>), dim3(grid), dim3(128), 0, stream,
-                       static_cast<const T*>(q), ws.khi, ws.klo, ws.inv_t, head_active, scores,
+                       static_cast<const T*>(q), ws.khi, ws.klo, ws.inv_t, head_active, nullptr, scores,
                        p.tokens, p.nb, NBp);
+  return hipGetLastError();
+}
+
+// Cluster centroids as pooled keys: kt = c * mul (one rounding), zero rows
+// and max 0 for empty clusters; one wave per (cluster, head).
+template <int D>
+__global__ __launch_bounds__(kWave) void cent_prep_kernel(const float* __restrict__ cent,
+                                                          const int* __restrict__ sizes, float* __restrict__ kt,
+                                                          float* __restrict__ bmax, int NB, double mul) {
+  const int j = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  const size_t row = static_cast<size_t>(h) * NB + j;
+  const bool live = sizes[row] > 0;
+  float a = 0.f;
+  for (int d = lane; d < D; d += kWave) {
+    const float x = live ? static_cast<float>(static_cast<double>(cent[row * D + d]) * mul) : 0.f;
+    kt[row * D + d] = x;
+    a = fmaxf(a, fabsf(x));
+  }
+  a = wave_max(a);
+  if (lane == 0) bmax[row] = a;
+}
+
+template <typename T, int D>
+hipError_t launch_cluster_scoring_t(const Problem& p, const void* q, const float* cent, const int* sizes,
+                                    float* scores, const ScoreWs& ws, hipStream_t stream) {
+  const int NBp = (p.nb + kScoreRowPad - 1) / kScoreRowPad * kScoreRowPad;
+  const double mul = static_cast<double>(p.scale) * 1.4426950408889634;
+  hipLaunchKernelGGL((cent_prep_kernel<D>), dim3(p.nb, p.heads), dim3(kWave), 0, stream, cent, sizes, ws.kt,
+                     ws.bmax, p.nb, mul);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((split_kernel<D>), dim3(kSplitGroups, p.heads), dim3(256), 0, stream,
+                     ws.kt, ws.bmax, nullptr, ws.khi, ws.klo, ws.inv_t, p.nb, NBp);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int grid = p.heads * p.nb;
+  if (p.block == 128)
+    hipLaunchKernelGGL((score_kernel<T, D, 128, 4, true>), dim3(grid), dim3(256), 0, stream,
+                       static_cast<const T*>(q), ws.khi, ws.klo, ws.inv_t, nullptr, sizes, scores, p.tokens,
+                       p.nb, NBp);
+  else
+    hipLaunchKernelGGL((score_kernel<T, D, 64, 4, true>), dim3(grid), dim3(128), 0, stream,
+                       static_cast<const T*>(q), ws.khi, ws.klo, ws.inv_t, nullptr, sizes, scores, p.tokens,
+                       p.nb, NBp);
   return hipGetLastError();
 }
 
@@ -498,6 +558,15 @@ hipError_t launch_scoring(const Problem& p, const void* q, const void* k,
   }
   return p.head_dim == 128 ? launch_scoring_t<float, 128>(p, q, k, head_active, scores, ws, stream)
                            : launch_scoring_t<float, 64>(p, q, k, head_active, scores, ws, stream);
+}
+
+hipError_t launch_cluster_scoring(const Problem& p, const void* q, const float* cent, const int* sizes,
+                                  float* scores, const ScoreWs& ws, hipStream_t stream) {
+  if (p.dtype == 0)
+    return p.head_dim == 128 ? launch_cluster_scoring_t<uint16_t, 128>(p, q, cent, sizes, scores, ws, stream)
+                             : launch_cluster_scoring_t<uint16_t, 64>(p, q, cent, sizes, scores, ws, stream);
+  return p.head_dim == 128 ? launch_cluster_scoring_t<float, 128>(p, q, cent, sizes, scores, ws, stream)
+                           : launch_cluster_scoring_t<float, 64>(p, q, cent, sizes, scores, ws, stream);
 }
 
 }  // namespace rsa

@@ -91,7 +91,8 @@ typedef enum {
   RSA_OP_ATTN = 3,
   RSA_OP_POOLED = 4, /* rsa_score_blocks_pooled */
   RSA_OP_GRAM = 5,   /* rsa_query_gram */
-  RSA_OP_KMEANS = 6  /* rsa_kmeans */
+  RSA_OP_KMEANS = 6, /* rsa_kmeans */
+  RSA_OP_CLUSTER_ATTN = 7 /* rsa_cluster_attn */
 } rsa_op;
 
 /*
@@ -354,6 +355,51 @@ rsa_status rsa_query_gram(const rsa_problem* p, const void* q, float* gram, void
 rsa_status rsa_kmeans(const rsa_problem* p, const void* k, const float* gram, int32_t iters, int32_t init,
                       float* centroids, int32_t* labels, int32_t* sizes, int32_t* order, void* ws,
                       size_t ws_bytes, hipStream_t stream);
+
+/*
+ * PARK scores with the clusters of rsa_kmeans as key blocks (PARK, Abstract:
+ * the clusters' mean representations serve block retrieval).  For query
+ * block I (contiguous, as everywhere) and cluster J:
+ *
+ *   scores[h,I,J] = (1/b_I) sum_{i in I} softmax_J'(scale * <q_i, centroids[h,J']>)[J],
+ *
+ * the softmax taken over the non-empty clusters J' (sizes[h,J'] > 0); an empty
+ * cluster scores 0.  Rows sum to 1, so rsa_select_topp applies unchanged and
+ * never needs an empty cluster before every live one.  q as in
+ * rsa_score_blocks; centroids [heads, NB, head_dim] fp32 and sizes [heads, NB]
+ * int32 as rsa_kmeans writes them; scores [heads, NB, NB] fp32, 16-byte
+ * aligned.  Arithmetic as rsa_score_blocks (centroid times scale*log2(e)
+ * rounded once to fp32, two fp16 terms on the matrix cores).  ws / ws_bytes:
+ * at least rsa_workspace_bytes(p, RSA_OP_SCORE) bytes, 256-byte aligned.
+ */
+rsa_status rsa_score_clusters(const rsa_problem* p, const void* q, const float* centroids, const int32_t* sizes,
+                              float* scores, void* ws, size_t ws_bytes, hipStream_t stream);
+
+/*
+ * Attention with the clusters of rsa_kmeans as key blocks (PARK, Abstract:
+ * attention computed only inside the retrieved blocks).  Row (h, I) of
+ * counts / block_idx lists clusters (e.g. rsa_select_topp on the scores of
+ * rsa_score_clusters), read as a set as in rsa_block_sparse_attn; empty
+ * clusters add nothing.  For query i of the contiguous query block I the
+ * visible keys are the keys of the listed clusters:
+ *
+ *   out[h,i,:] = sum_{t : labels[h,t] listed} softmax_t(scale * <q_i, k_t>) v_t,
+ *
+ * and lse as in rsa_block_sparse_attn (a row with no key: out 0, lse -inf).
+ * sizes, order: as rsa_kmeans writes them.  q, k, v, out, lse as in
+ * rsa_block_sparse_attn.  The call gathers k and v into cluster order (each
+ * cluster padded with zeros to whole 32-key sub-tiles), turns each row's list
+ * into a table of sub-tiles and runs the block-sparse attention kernel over
+ * the tables (bf16: matrix cores as rsa_block_sparse_attn; fp32: fp32 FMA).
+ * ws / ws_bytes: at least rsa_workspace_bytes(p, RSA_OP_CLUSTER_ATTN) bytes,
+ * 256-byte aligned: padded k and v (bf16: v transposed), Np = tokens +
+ * 31 * NB rounded up to 32 keys per head; cluster starts; per-row sub-tile
+ * counts and tables of Np / 32 entries.
+ * Non-finite values in q, k or v give undefined results.
+ */
+rsa_status rsa_cluster_attn(const rsa_problem* p, const void* q, const void* k, const void* v, const int32_t* sizes,
+                            const int32_t* order, const int32_t* counts, const int32_t* block_idx, void* out,
+                            float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
 #ifdef __cplusplus
 }

@@ -43,7 +43,8 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"rsa_workspace_bytes", "rsa_status_str", "rsa_version", "rsa_score_blocks",
                           "rsa_select_topp", "rsa_mask_drift", "rsa_block_sparse_attn",
                           "rsa_dense_block_mass", "rsa_score_blocks_pooled", "rsa_attn_omitted",
-                          "rsa_attn_merge", "rsa_query_gram", "rsa_kmeans"}
+                          "rsa_attn_merge", "rsa_query_gram", "rsa_kmeans",
+                          "rsa_score_clusters", "rsa_cluster_attn"}
     for n in names:
         assert hasattr(lib, n), n
 
@@ -77,6 +78,11 @@ def test_workspace_sizes():
     assert B.workspace_bytes(p, B.OP_KMEANS) == (2 * al(2 * 40 * nbp * 128) + al(4 * 40 * nbp * 128)
                                                  + al(4 * 40 * nbp) + al(4 * 40 * 591) + al(4 * 40 * nch * 591)
                                                  + al(4 * 40 * 75600) + al(4 * 40 * 591))
+    # cluster attention: k and v in the padded cluster layout, starts, sub-tile tables
+    npad = -(-(75600 + 31 * 591) // 32) * 32
+    rows = 40 * 591
+    assert B.workspace_bytes(p, B.OP_CLUSTER_ATTN) == (2 * al(2 * 40 * npad * 128) + 3 * al(4 * rows)
+                                                       + al(4 * rows * (npad // 32)))
     # query-pooled scorer: pooled q and k, then block maxima
     assert B.workspace_bytes(p, B.OP_POOLED) == 2 * al(4 * 40 * 591 * 128) + al(4 * 40 * 591)
     assert B.workspace_bytes(prob(d=96), B.OP_SCORE) == 0          # invalid problem -> 0
@@ -127,6 +133,9 @@ def test_null_problem_and_pointers(lib):
     assert lib.rsa_attn_merge(ctypes.byref(p), b.ptr, b.ptr, b.ptr, None, None) == NULL
     assert lib.rsa_attn_merge(None, b.ptr, b.ptr, b.ptr, b.ptr, None) == NULL
     assert lib.rsa_query_gram(ctypes.byref(p), None, b.ptr, b.ptr, 1 << 30, None) == NULL
+    assert lib.rsa_score_clusters(ctypes.byref(p), b.ptr, b.ptr, None, b.ptr, b.ptr, 1 << 30, None) == NULL
+    assert lib.rsa_cluster_attn(ctypes.byref(p), b.ptr, b.ptr, b.ptr, b.ptr, None, b.ptr, b.ptr, b.ptr, b.ptr,
+                                b.ptr, 1 << 30, None) == NULL
     assert lib.rsa_kmeans(ctypes.byref(p), b.ptr, b.ptr, 3, 1, b.ptr, b.ptr, None, b.ptr, b.ptr, 1 << 30,
                           None) == NULL
     assert b.untouched()

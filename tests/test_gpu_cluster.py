@@ -150,3 +150,125 @@ def test_kmeans_all_keys_equal():
     assert (host(order) == np.arange(wl.tokens)[None, :]).all()
     want = inp.k[:, 0, :].float()
     assert torch.equal(cent.cpu(), want[:, None, :].expand(-1, wl.nblocks, -1))
+
+
+# (rel L2, max abs) on outputs, max abs on lse: as for block-sparse attention
+ATTN_TOL = {"bf16": (1e-2, 3e-2, 1e-3), "fp32": (1e-4, 1e-4, 1e-4)}
+
+
+def rel_l2(a, b):
+    return float(np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300))
+
+
+def clustered(c, iters=3):
+    if not hasattr(c, "cl"):
+        c.cl = R.kmeans(c.k, c.gram, c.p, iters=iters)
+        c.v = W.make_inputs(c.wl).v.to(DEV).contiguous()
+        c.v64 = W.to_f64(c.v.cpu())
+        torch.cuda.synchronize()
+    return c.cl
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_cluster_scores_match_oracle(name):
+    c = case(name)
+    wl = c.wl
+    cent, labels, sizes, order = clustered(c)
+    sz = sizes.clone()
+    sz[:, 3] = 0                                   # one cluster taken as empty
+    for s_in in (sizes, sz):
+        S = host(R.score_clusters(c.q, cent, s_in, c.p)).astype(np.float64)
+        cg, si = host(cent).astype(np.float64), host(s_in)
+        for h in range(wl.heads):
+            want = O.cluster_scores(c.q64[h], cg[h], si[h], wl.block)
+            err = np.abs(S[h] - want).max()
+            say(f"[gpu] cluster scores {name} h={h} empty={int((si[h] == 0).sum())}: max |dS| {err:.2e}")
+            assert err <= 1e-6
+            assert (S[h][:, si[h] == 0] == 0).all()
+            np.testing.assert_allclose(S[h].sum(axis=1), 1.0, atol=1e-5)
+
+
+def _set_lists(heads, nb, sizes, seed):
+    """Cluster lists as sets: shuffled, repeats, out-of-range entries; row 0
+    empty, the last row every cluster with an over-long count."""
+    rng = np.random.default_rng(seed)
+    counts = np.zeros((heads, nb), np.int32)
+    idx = np.full((heads, nb, nb), -1, np.int32)
+    lists = []
+    for h in range(heads):
+        rows = []
+        for i in range(nb):
+            if i == 0:
+                lst = []
+            elif i == nb - 1:
+                lst = list(rng.permutation(nb))
+            else:
+                lst = list(rng.choice(nb, int(rng.integers(1, nb)), replace=False))
+                lst += [lst[0]] * int(rng.integers(0, 2)) + [nb + 5, -1][: int(rng.integers(0, 3))]
+                lst = lst[:nb]
+                rng.shuffle(lst)
+            counts[h, i] = len(lst) if i != nb - 1 else nb + 3
+            idx[h, i, :len(lst)] = lst
+            rows.append([j for j in lst if 0 <= j < nb])
+        lists.append(rows)
+    return counts, idx, lists
+
+
+def _check_attn(name, tag, out, lse, want_o, want_l, dtype):
+    tol_l2, tol_abs, tol_lse = ATTN_TOL[dtype]
+    empty = np.isneginf(want_l)
+    assert (np.isneginf(lse) == empty).all() and (out[empty] == 0).all()
+    live = ~empty
+    e = (rel_l2(out[live], want_o[live]), np.abs(out[live] - want_o[live]).max(),
+         np.abs(lse[live] - want_l[live]).max())
+    say(f"[gpu] cluster attention {name} {tag}: rel-l2 {e[0]:.2e} max-abs {e[1]:.2e} lse {e[2]:.2e}")
+    assert e[0] <= tol_l2 and e[1] <= tol_abs and e[2] <= tol_lse
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_cluster_attention_matches_oracle(name):
+    c = case(name)
+    wl = c.wl
+    cent, labels, sizes, order = clustered(c)
+    lab = host(labels)
+    cnt, ix, lists = _set_lists(wl.heads, wl.nblocks, host(sizes), 400 + sorted(CASES).index(name))
+    out, lse = R.cluster_attn(c.q, c.k, c.v, sizes, order, torch.from_numpy(cnt).to(DEV),
+                              torch.from_numpy(ix).to(DEV), c.p)
+    o, l = host(out.float()).astype(np.float64), host(lse).astype(np.float64)
+    for h in range(wl.heads):
+        want_o, want_l = O.cluster_attention(c.q64[h], c.k64[h], c.v64[h], wl.block, lab[h], lists[h])
+        _check_attn(name, f"set lists h={h}", o[h], l[h], want_o, want_l, wl.dtype)
+    # the retrieval path: cluster scores -> top-p -> cluster attention
+    S = R.score_clusters(c.q, cent, sizes, c.p)
+    top_p = torch.full((wl.heads,), 0.9, dtype=torch.float32, device=DEV)
+    _, counts, idx, dens = R.select_topp(S, top_p, c.p)
+    out, lse = R.cluster_attn(c.q, c.k, c.v, sizes, order, counts, idx, c.p)
+    o, l = host(out.float()).astype(np.float64), host(lse).astype(np.float64)
+    cn, ixn = host(counts), host(idx)
+    for h in range(wl.heads):
+        sel = [ixn[h, i, :cn[h, i]] for i in range(wl.nblocks)]
+        want_o, want_l = O.cluster_attention(c.q64[h], c.k64[h], c.v64[h], wl.block, lab[h], sel)
+        _check_attn(name, f"top-p h={h} density {float(host(dens)[h]):.3f}", o[h], l[h], want_o, want_l, wl.dtype)
+
+
+def test_contiguous_clusters_equal_block_attention():
+    """Clusters that are the contiguous blocks (labels t // B): cluster
+    attention on any list equals block-sparse attention on the same list."""
+    c = case("bf16_d128_b64")
+    clustered(c)
+    wl, p = c.wl, c.p
+    nb, b = wl.nblocks, wl.block
+    sizes = torch.tensor([[min(b, wl.tokens - j * b) for j in range(nb)]] * wl.heads, dtype=torch.int32,
+                         device=DEV)
+    order = torch.arange(wl.tokens, dtype=torch.int32, device=DEV).repeat(wl.heads, 1).contiguous()
+    cnt, ix, _ = _set_lists(wl.heads, nb, None, 450)
+    cnt_t, ix_t = torch.from_numpy(cnt).to(DEV), torch.from_numpy(ix).to(DEV)
+    o1, l1 = R.cluster_attn(c.q, c.k, c.v, sizes, order, cnt_t, ix_t, p)
+    o2, l2 = R.block_sparse_attn(c.q, c.k, c.v, cnt_t, ix_t, p)
+    torch.cuda.synchronize()
+    a, bb = host(o1.float()).astype(np.float64), host(o2.float()).astype(np.float64)
+    assert rel_l2(a, bb) <= 2e-3 and np.abs(a - bb).max() <= 1e-2
+    la, lb = host(l1), host(l2)
+    assert (np.isneginf(la) == np.isneginf(lb)).all()
+    live = np.isfinite(lb)
+    assert np.abs(la[live] - lb[live]).max() <= 1e-5
