@@ -50,6 +50,9 @@ def parse():
     ap.add_argument("--correction", action="store_true",
                     help="report the cached correction over a drifting trajectory instead")
     ap.add_argument("--traj-steps", type=int, default=8, help="trajectory length for --correction")
+    ap.add_argument("--clusters", action="store_true",
+                    help="report PARK's query-aware key clusters against contiguous blocks instead")
+    ap.add_argument("--kmeans-iters", type=int, default=5, help="Lloyd iterations for --clusters")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -333,6 +336,110 @@ def correction(args):
     print(json.dumps(res), flush=True)
 
 
+def clusters(args):
+    """PARK's query-aware key clusters as key blocks against contiguous blocks
+    (PARK, Abstract).
+
+    On one workload: the Gram matrix of the queries, ``--kmeans-iters`` Lloyd
+    iterations in its metric, the cluster scores and the cluster attention are
+    timed with HIP events on the library's stream, beside the contiguous-block
+    scorer and attention.  For a sweep of top-p thresholds both paths select
+    with rsa_select_topp and attend; each reports its key density (selected
+    keys over all keys, mean over queries) and the relative L2 error of its
+    output against dense attention (the attention call given every block).
+    """
+    import numpy as np
+    import torch
+    import workloads as W
+    import block_sparse_attention_scoring_amd as R
+
+    wl = W.CONFIGS[args.workload]
+    inp = W.make_inputs(wl)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    stream = torch.cuda.current_stream(dev)
+    q, k, v = inp.q.to(dev), inp.k.to(dev), inp.v.to(dev)
+    p = R.make_problem(q, wl.grid, wl.block)
+    nb, H, N, b = wl.nblocks, wl.heads, wl.tokens, wl.block
+
+    def timed(fn, reps=3):
+        fn()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(reps):
+            fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1) / reps
+
+    ws_g = torch.empty(max(1, R.workspace_bytes(p, R.OP_GRAM)), dtype=torch.uint8, device=dev)
+    ws_k = torch.empty(max(1, R.workspace_bytes(p, R.OP_KMEANS)), dtype=torch.uint8, device=dev)
+    ws_s = torch.empty(max(1, R.workspace_bytes(p, R.OP_SCORE)), dtype=torch.uint8, device=dev)
+    ws_a = torch.empty(max(1, R.workspace_bytes(p, R.OP_ATTN)), dtype=torch.uint8, device=dev)
+    ws_c = torch.empty(max(1, R.workspace_bytes(p, R.OP_CLUSTER_ATTN)), dtype=torch.uint8, device=dev)
+    gram = R.query_gram(q, p, workspace=ws_g)
+    cent, labels, sizes, order = R.kmeans(k, gram, p, iters=args.kmeans_iters, workspace=ws_k)
+    t_gram = timed(lambda: R.query_gram(q, p, out=gram, workspace=ws_g))
+    t_km = timed(lambda: R.kmeans(k, gram, p, iters=args.kmeans_iters, centroids=cent, labels=labels,
+                                  sizes=sizes, order=order, workspace=ws_k), reps=2)
+    S_c = R.score_clusters(q, cent, sizes, p, workspace=ws_s)
+    S_b = R.score_blocks(q, k, p, workspace=ws_s)
+    t_sc = timed(lambda: R.score_clusters(q, cent, sizes, p, out=S_c, workspace=ws_s))
+    t_sb = timed(lambda: R.score_blocks(q, k, p, out=S_b, workspace=ws_s))
+    full_c = torch.full((H, nb), nb, dtype=torch.int32, device=dev)
+    full_i = torch.arange(nb, dtype=torch.int32, device=dev).repeat(H, nb, 1).contiguous()
+    dense, _ = R.block_sparse_attn(q, k, v, full_c, full_i, p, want_lse=False, workspace=ws_a)
+    dn = dense.float().flatten(1).norm(dim=1)
+    sz = sizes.cpu().numpy().astype(np.int64)
+    bsz = np.full(nb, b, np.int64)
+    bsz[-1] = N - b * (nb - 1)
+    qb = bsz.astype(np.float64)                     # queries per query block
+
+    def density(counts, idx, key_sizes):
+        c, ix = counts.cpu().numpy(), idx.cpu().numpy()
+        keep = np.arange(nb)[None, None, :] < c[..., None]
+        keys = np.where(keep, np.take_along_axis(key_sizes[:, None, :].repeat(nb, 1), np.clip(ix, 0, nb - 1), 2),
+                        0).sum(-1)                  # [H, NB] selected keys per query block
+        return float((keys * qb[None, :]).sum() / (H * N * N)), float(4 * wl.head_dim * (keys * qb[None, :]).sum())
+
+    sweep = []
+    t_cattn = t_battn = None
+    for tp in (0.5, 0.7, 0.8, 0.9, 0.95):
+        top_p = torch.full((H,), tp, dtype=torch.float32, device=dev)
+        row = {"top_p": tp}
+        for name, S, fn, key_sizes in (
+                ("blocks", S_b, lambda c, i, o: R.block_sparse_attn(q, k, v, c, i, p, out=o, want_lse=False,
+                                                                    workspace=ws_a), bsz[None, :].repeat(H, 0)),
+                ("clusters", S_c, lambda c, i, o: R.cluster_attn(q, k, v, sizes, order, c, i, p, out=o,
+                                                                 want_lse=False, workspace=ws_c), sz)):
+            _, counts, idx, _ = R.select_topp(S, top_p, p)
+            out = torch.empty_like(q)
+            fn(counts, idx, out)
+            err = ((out.float() - dense.float()).flatten(1).norm(dim=1) / dn).cpu().numpy()
+            dens, flops = density(counts, idx, key_sizes)
+            row[name] = {"density": round(dens, 4), "rel_err": round(float(err.mean()), 5)}
+            if abs(tp - 0.9) < 1e-9:
+                t = timed(lambda: fn(counts, idx, out))
+                row[name]["attn_ms"] = round(t, 3)
+                row[name]["attn_tflops"] = round(flops / (t * 1e-3) / 1e12, 1)
+            del out
+        sweep.append(row)
+        print(json.dumps({"progress": row}), file=sys.stderr, flush=True)
+    res = {
+        "mode": "clusters",
+        "metric": "relative L2 error against dense attention at the key density each selection gives",
+        "workload": wl.name, "heads": H, "tokens": N, "block": b, "kmeans_iters": args.kmeans_iters,
+        "data": "synthetic (seeded smooth 3-D field + noise; no weights)",
+        "non_empty_clusters_mean": round(float((sz > 0).sum(1).mean()), 1),
+        "cluster_size_max": int(sz.max()),
+        "ms": {"query_gram": round(t_gram, 3), "kmeans": round(t_km, 3), "score_clusters": round(t_sc, 3),
+               "score_blocks": round(t_sb, 3)},
+        "sweep": sweep,
+    }
+    print(json.dumps(res), flush=True)
+
+
 def main():
     args = parse()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -348,6 +455,9 @@ def main():
         return
     if args.correction:
         correction(args)
+        return
+    if args.clusters:
+        clusters(args)
         return
 
     import numpy as np

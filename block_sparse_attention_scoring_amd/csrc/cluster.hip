@@ -23,7 +23,8 @@
 //             histograms and in-chunk ranks, a scan over chunks and clusters,
 //             a scatter), deterministic, no floating-point atomics;
 //     means   each non-empty cluster's centroid = mean of its keys in sorted
-//             order (fp64 sums, one rounding); an empty cluster keeps its own.
+//             order (fp64 sums over fixed segments of the order, segments
+//             added in order, one rounding); an empty cluster keeps its own.
 #include "common.h"
 #include "kernels.h"
 
@@ -34,6 +35,7 @@ constexpr int kGramChunk = 2048;  // tokens per partial Gram matrix
 constexpr int kGramStage = 64;    // tokens staged in LDS at a time
 constexpr int kHistChunk = 256;   // tokens per histogram chunk
 constexpr int kAssignRows = 128;  // keys per assignment workgroup
+constexpr int kSeg = 256;         // sorted positions per mean segment
 
 // ---------------------------------------------------------------- gram
 // Partial Q^T Q of one chunk of kGramChunk tokens, bf16 input.  The chunk is
@@ -186,17 +188,34 @@ __global__ __launch_bounds__(256) void assign_bf16_kernel(const uint16_t* __rest
   const uint16_t* wl = wlo + static_cast<size_t>(h) * NBp * D;
   float best = -INFINITY;
   int bj = 0;
+  // the next chunk is loaded into registers while this one is multiplied
+  constexpr int kPerThread = 32 * kCpr / 256;
+  static_assert(32 * kCpr % 256 == 0, "chunk not divisible");
+  u32x4 nh[kPerThread], nl[kPerThread];
+  float nb = 0.f;
+  auto fetch = [&](int c) {
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int e = tid + 256 * i, r = e / kCpr, ch = e % kCpr;
+      const size_t g = (static_cast<size_t>(32 * c + r) * D) + ch * 8;
+      nh[i] = *reinterpret_cast<const u32x4*>(wh + g);
+      nl[i] = *reinterpret_cast<const u32x4*>(wl + g);
+    }
+    if (tid < 32) nb = bvec[static_cast<size_t>(h) * NBp + 32 * c + tid];
+  };
+  fetch(0);
   for (int c = 0; c < NBp / 32; ++c) {
     __syncthreads();
-    for (int e = tid; e < 32 * kCpr; e += 256) {
-      const int r = e / kCpr, ch = e % kCpr;
-      const size_t g = (static_cast<size_t>(32 * c + r) * D) + ch * 8;
+#pragma unroll
+    for (int i = 0; i < kPerThread; ++i) {
+      const int e = tid + 256 * i, r = e / kCpr, ch = e % kCpr;
       const int dst = r * D + (ch ^ swz<kCpr>(r)) * 8;
-      *reinterpret_cast<u32x4*>(&th[dst]) = *reinterpret_cast<const u32x4*>(wh + g);
-      *reinterpret_cast<u32x4*>(&tl[dst]) = *reinterpret_cast<const u32x4*>(wl + g);
+      *reinterpret_cast<u32x4*>(&th[dst]) = nh[i];
+      *reinterpret_cast<u32x4*>(&tl[dst]) = nl[i];
     }
-    if (tid < 32) bs[tid] = bvec[static_cast<size_t>(h) * NBp + 32 * c + tid];
+    if (tid < 32) bs[tid] = nb;
     __syncthreads();
+    if (c + 1 < NBp / 32) fetch(c + 1);
     f32x16 ah = f32x16{}, al = f32x16{};
 #pragma unroll
     for (int s = 0; s < kKS; ++s) {
@@ -267,25 +286,30 @@ __global__ __launch_bounds__(kHistChunk) void hist_kernel(const int* __restrict_
   for (int j = tid; j < NB; j += kHistChunk) dst[j] = cnt[j];
 }
 
-// Per head: turn the chunk histograms into each chunk's first rank per
-// cluster (exclusive over chunks, in place), the cluster sizes, and each
-// cluster's first position in the sorted order (exclusive over clusters).
-__global__ __launch_bounds__(256) void scan_kernel(int* __restrict__ hist, int* __restrict__ sizes,
-                                                   int* __restrict__ offs, int NB, int nch) {
+// One thread per (cluster, head): the chunk histograms become each chunk's
+// first rank in the cluster (exclusive over chunks, in place); the total is
+// the cluster's size.
+__global__ __launch_bounds__(64) void chunk_scan_kernel(int* __restrict__ hist, int* __restrict__ sizes, int NB,
+                                                        int nch) {
+  const int h = blockIdx.y, j = blockIdx.x * 64 + threadIdx.x;
+  if (j >= NB) return;
+  int* p = hist + static_cast<size_t>(h) * nch * NB + j;
+  int run = 0;
+  for (int c = 0; c < nch; ++c) {
+    const int v = p[static_cast<size_t>(c) * NB];
+    p[static_cast<size_t>(c) * NB] = run;
+    run += v;
+  }
+  sizes[static_cast<size_t>(h) * NB + j] = run;
+}
+
+// Per head: each cluster's first position in the sorted order (exclusive
+// sum of the sizes over clusters).
+__global__ __launch_bounds__(256) void scan_kernel(const int* __restrict__ sizes, int* __restrict__ offs, int NB) {
   __shared__ int sz[kMaxClusters];
   __shared__ int part[256];
   const int h = blockIdx.x, tid = threadIdx.x;
-  for (int j = tid; j < NB; j += 256) {
-    int run = 0;
-    for (int c = 0; c < nch; ++c) {
-      int* p = hist + (static_cast<size_t>(h) * nch + c) * NB + j;
-      const int v = *p;
-      *p = run;
-      run += v;
-    }
-    sz[j] = run;
-    sizes[static_cast<size_t>(h) * NB + j] = run;
-  }
+  for (int j = tid; j < NB; j += 256) sz[j] = sizes[static_cast<size_t>(h) * NB + j];
   __syncthreads();
   constexpr int kPer = kMaxClusters / 256;  // clusters per thread in the scan
   int local = 0;
@@ -330,62 +354,87 @@ __global__ __launch_bounds__(kHistChunk) void scatter_kernel(const int* __restri
 }
 
 // ---------------------------------------------------------------- means
-template <typename T>
-__device__ __forceinline__ void load8f(const T* src, float (&x)[8]);
-template <>
-__device__ __forceinline__ void load8f<uint16_t>(const uint16_t* src, float (&x)[8]) {
-  const u32x4 raw = *reinterpret_cast<const u32x4*>(src);
-#pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[2 * e] = __uint_as_float(raw[e] << 16);
-    x[2 * e + 1] = __uint_as_float(raw[e] & 0xffff0000u);
+// Cluster means over the sorted order, cut into segments of kSeg positions
+// so that a large cluster does not rest on one workgroup.  One workgroup per
+// (segment, head), one thread per dim, the segment's keys in sorted order,
+// fp64 sums: a cluster that lies inside the segment gets its mean at once;
+// the first and the last run of the segment (which may continue into the
+// neighbours) leave their sums in part[h, seg, 0 / 1] for seg_combine_kernel.
+template <typename T, int D>
+__global__ __launch_bounds__(D) void seg_sum_kernel(const T* __restrict__ k, const int* __restrict__ order,
+                                                    const int* __restrict__ labels, const int* __restrict__ sizes,
+                                                    const int* __restrict__ offs, double* __restrict__ part,
+                                                    float* __restrict__ cent, int N, int NB, int nseg) {
+  __shared__ int tok[kSeg];
+  __shared__ int lab[kSeg];
+  const int sg = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+  const int p0 = sg * kSeg, len = min(kSeg, N - p0);
+  for (int i = d; i < len; i += D) {
+    const int t = order[static_cast<size_t>(h) * N + p0 + i];
+    tok[i] = t;
+    lab[i] = labels[static_cast<size_t>(h) * N + t];
   }
-}
-template <>
-__device__ __forceinline__ void load8f<float>(const float* src, float (&x)[8]) {
-  const f32x4 a = *reinterpret_cast<const f32x4*>(src);
-  const f32x4 b = *reinterpret_cast<const f32x4*>(src + 4);
+  __syncthreads();
+  const T* kh = k + static_cast<size_t>(h) * N * D + d;
+  double acc = 0.0;
+  int first = 1;
+  constexpr int kBatch = 16;  // loads in flight per thread
+  for (int i0 = 0; i0 < len; i0 += kBatch) {
+    float xb[kBatch];
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    x[e] = a[e];
-    x[4 + e] = b[e];
+    for (int u = 0; u < kBatch; ++u) {
+      const int i = min(i0 + u, len - 1);
+      if constexpr (sizeof(T) == 2)
+        xb[u] = __uint_as_float(static_cast<uint32_t>(kh[static_cast<size_t>(tok[i]) * D]) << 16);
+      else
+        xb[u] = kh[static_cast<size_t>(tok[i]) * D];
+    }
+    for (int u = 0; u < kBatch && i0 + u < len; ++u) {
+      const int i = i0 + u;
+      acc += static_cast<double>(xb[u]);
+      const int j = lab[i];
+      if (i + 1 == len || lab[i + 1] != j) {  // end of a run
+        const size_t row = static_cast<size_t>(h) * NB + j;
+        const int off = offs[row], n = sizes[row];
+        if (off >= p0 && off + n <= p0 + len) {
+          cent[row * D + d] = static_cast<float>(acc / n);
+        } else {
+          double* ps = part + (static_cast<size_t>(h) * nseg + sg) * 2 * D + d;
+          if (first) ps[0] = acc;
+          if (i + 1 == len) ps[D] = acc;
+        }
+        acc = 0.0;
+        first = 0;
+      }
+    }
   }
 }
 
-// One workgroup per (cluster, head): the mean of the cluster's keys, visited
-// in sorted order by 256/(D/8) row groups, fp64 sums added in group order.
-template <typename T, int D>
-__global__ __launch_bounds__(256) void means_kernel(const T* __restrict__ k, const int* __restrict__ order,
-                                                    const int* __restrict__ sizes, const int* __restrict__ offs,
-                                                    float* __restrict__ cent, int N, int NB) {
-  constexpr int kLanes = D / 8, kGroups = 256 / kLanes;
-  __shared__ double part[kGroups][D];
-  const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const int n = sizes[static_cast<size_t>(h) * NB + j];
-  if (n == 0) return;  // an empty cluster keeps its centroid
-  const int* ord = order + static_cast<size_t>(h) * N + offs[static_cast<size_t>(h) * NB + j];
-  const int rg = tid / kLanes, c8 = (tid % kLanes) * 8;
-  double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
-  for (int r = rg; r < n; r += kGroups) {
-    float x[8];
-    load8f<T>(k + (static_cast<size_t>(h) * N + ord[r]) * D + c8, x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[e] += static_cast<double>(x[e]);
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) part[rg][c8 + e] = acc[e];
-  __syncthreads();
-  if (tid < D) {
-    double s = 0.0;
-    for (int g = 0; g < kGroups; ++g) s += part[g][tid];
-    cent[(static_cast<size_t>(h) * NB + j) * D + tid] = static_cast<float>(s / n);
-  }
+// Clusters spanning several segments: their last-run sum in the first
+// segment, whole middle segments, the first-run sum in the last segment,
+// added in segment order.
+template <int D>
+__global__ __launch_bounds__(D) void seg_combine_kernel(const double* __restrict__ part,
+                                                        const int* __restrict__ sizes, const int* __restrict__ offs,
+                                                        float* __restrict__ cent, int NB, int nseg) {
+  const int j = blockIdx.x, h = blockIdx.y, d = threadIdx.x;
+  const size_t row = static_cast<size_t>(h) * NB + j;
+  const int n = sizes[row], off = offs[row];
+  if (n == 0) return;
+  const int s0 = off / kSeg, s1 = (off + n - 1) / kSeg;
+  if (s0 == s1) return;  // done by seg_sum_kernel
+  const double* ph = part + static_cast<size_t>(h) * nseg * 2 * D + d;
+  double acc = ph[(static_cast<size_t>(s0) * 2 + 1) * D];
+  for (int sg = s0 + 1; sg < s1; ++sg) acc += ph[static_cast<size_t>(sg) * 2 * D];
+  acc += ph[static_cast<size_t>(s1) * 2 * D];
+  cent[row * D + d] = static_cast<float>(acc / n);
 }
 
 struct KmeansWs {
   uint16_t *whi, *wlo;
   float *w32, *bvec, *bmax;
   int *hist, *rank, *offs;
+  double* part;
   size_t total;
 };
 
@@ -395,15 +444,17 @@ KmeansWs kmeans_ws_layout(const Problem& p, void* base) {
   const size_t NBp = (p.nb + 31) / 32 * 32;
   const size_t nch = (p.tokens + kHistChunk - 1) / kHistChunk;
   const size_t H = p.heads, D = p.head_dim;
+  const size_t nseg = (p.tokens + kSeg - 1) / kSeg;
   const size_t sizes[] = {al256(2 * H * NBp * D), al256(2 * H * NBp * D), al256(4 * H * NBp * D),
                           al256(4 * H * NBp), al256(4 * H * p.nb), al256(4 * H * nch * p.nb),
-                          al256(4 * H * static_cast<size_t>(p.tokens)), al256(4 * H * p.nb)};
+                          al256(4 * H * static_cast<size_t>(p.tokens)), al256(4 * H * p.nb),
+                          al256(8 * H * nseg * 2 * D)};
   KmeansWs w{};
   char* b = static_cast<char*>(base);
   size_t off = 0;
-  void** ptrs[] = {(void**)&w.whi, (void**)&w.wlo, (void**)&w.w32, (void**)&w.bvec,
-                   (void**)&w.bmax, (void**)&w.hist, (void**)&w.rank, (void**)&w.offs};
-  for (int i = 0; i < 8; ++i) {
+  void** ptrs[] = {(void**)&w.whi, (void**)&w.wlo, (void**)&w.w32, (void**)&w.bvec, (void**)&w.bmax,
+                   (void**)&w.hist, (void**)&w.rank, (void**)&w.offs, (void**)&w.part};
+  for (int i = 0; i < 9; ++i) {
     if (b != nullptr) *ptrs[i] = b + off;
     off += sizes[i];
   }
@@ -419,6 +470,7 @@ hipError_t launch_kmeans_t(const Problem& p, const void* k, const float* gram, i
   const KmeansWs w = kmeans_ws_layout(p, ws);
   const int NB = p.nb, NBp = (p.nb + 31) / 32 * 32, N = p.tokens, H = p.heads;
   const int nch = (N + kHistChunk - 1) / kHistChunk;
+  const int nseg = (N + kSeg - 1) / kSeg;
   hipError_t e;
   if (init) {
     e = launch_block_means(p, k, 1.0, cent, w.bmax, stream);
@@ -437,17 +489,22 @@ hipError_t launch_kmeans_t(const Problem& p, const void* k, const float* gram, i
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(hist_kernel, dim3(nch, H), dim3(kHistChunk), 0, stream, labels, w.hist, w.rank, N, NB, nch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    hipLaunchKernelGGL(scan_kernel, dim3(H), dim3(256), 0, stream, w.hist, sizes, w.offs, NB, nch);
+    hipLaunchKernelGGL(chunk_scan_kernel, dim3((NB + 63) / 64, H), dim3(64), 0, stream, w.hist, sizes, NB, nch);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL(scan_kernel, dim3(H), dim3(256), 0, stream, sizes, w.offs, NB);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     hipLaunchKernelGGL(scatter_kernel, dim3(nch, H), dim3(kHistChunk), 0, stream, labels, w.hist, w.rank, w.offs,
                        order, N, NB, nch);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (p.dtype == 0)
-      hipLaunchKernelGGL((means_kernel<uint16_t, D>), dim3(NB, H), dim3(256), 0, stream,
-                         static_cast<const uint16_t*>(k), order, sizes, w.offs, cent, N, NB);
+      hipLaunchKernelGGL((seg_sum_kernel<uint16_t, D>), dim3(nseg, H), dim3(D), 0, stream,
+                         static_cast<const uint16_t*>(k), order, labels, sizes, w.offs, w.part, cent, N, NB, nseg);
     else
-      hipLaunchKernelGGL((means_kernel<float, D>), dim3(NB, H), dim3(256), 0, stream, static_cast<const float*>(k),
-                         order, sizes, w.offs, cent, N, NB);
+      hipLaunchKernelGGL((seg_sum_kernel<float, D>), dim3(nseg, H), dim3(D), 0, stream, static_cast<const float*>(k),
+                         order, labels, sizes, w.offs, w.part, cent, N, NB, nseg);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    hipLaunchKernelGGL((seg_combine_kernel<D>), dim3(NB, H), dim3(D), 0, stream, w.part, sizes, w.offs, cent, NB,
+                       nseg);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
