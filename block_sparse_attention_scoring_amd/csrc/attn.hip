@@ -585,43 +585,70 @@ hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const v
 // lies inside one cluster.
 
 // Per head: pstart (exclusive sum of the padded sizes) and ostart (exclusive
-// sum of the sizes: where the cluster starts in `order`).
+// sum of the sizes: where the cluster starts in `order`), and the sizes as
+// used (csize): each clamped to [0, N - ostart] so that the layout stays
+// inside its buffers whatever the caller passes.
 __global__ __launch_bounds__(256) void cl_scan_kernel(const int* __restrict__ sizes, int* __restrict__ pstart,
-                                                      int* __restrict__ ostart, int NB) {
+                                                      int* __restrict__ ostart, int* __restrict__ csize, int NB,
+                                                      int N) {
   constexpr int kPer = kMaxNB / 256;
   __shared__ int2 part[256];
   const int h = blockIdx.x, tid = threadIdx.x;
   const int* sz = sizes + static_cast<size_t>(h) * NB;
-  int2 local = make_int2(0, 0);
+  // pass 1: unclamped key counts per thread's clusters (64-bit: any input)
+  long long local = 0;
   for (int e = 0; e < kPer; ++e) {
     const int j = tid * kPer + e;
-    if (j < NB) {
-      const int n = max(sz[j], 0);
-      local.x += (n + 31) & ~31;
-      local.y += n;
-    }
+    if (j < NB) local += max(sz[j], 0);
   }
-  part[tid] = local;
+  __shared__ long long opart[256];
+  opart[tid] = local;
   __syncthreads();
   if (tid == 0) {
-    int2 run = make_int2(0, 0);
+    long long run = 0;
     for (int i = 0; i < 256; ++i) {
-      const int2 v = part[i];
-      part[i] = run;
-      run.x += v.x;
-      run.y += v.y;
+      const long long v = opart[i];
+      opart[i] = run;
+      run += v;
     }
   }
   __syncthreads();
-  int2 run = part[tid];
+  // pass 2: clamp against the keys left, then the padded starts
+  long long orun = opart[tid];
+  int plocal = 0;
   for (int e = 0; e < kPer; ++e) {
     const int j = tid * kPer + e;
     if (j < NB) {
-      pstart[static_cast<size_t>(h) * NB + j] = run.x;
-      ostart[static_cast<size_t>(h) * NB + j] = run.y;
-      const int n = max(sz[j], 0);
-      run.x += (n + 31) & ~31;
-      run.y += n;
+      const long long left = orun < N ? N - orun : 0;
+      const int n = static_cast<int>(min(static_cast<long long>(max(sz[j], 0)), left));
+      plocal += (n + 31) & ~31;
+      orun += max(sz[j], 0);
+    }
+  }
+  part[tid] = make_int2(plocal, 0);
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int v = part[i].x;
+      part[i].x = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  int prun = part[tid].x;
+  orun = opart[tid];
+  for (int e = 0; e < kPer; ++e) {
+    const int j = tid * kPer + e;
+    if (j < NB) {
+      const long long left = orun < N ? N - orun : 0;
+      const int n = static_cast<int>(min(static_cast<long long>(max(sz[j], 0)), left));
+      const size_t o = static_cast<size_t>(h) * NB + j;
+      pstart[o] = prun;
+      ostart[o] = static_cast<int>(min(orun, static_cast<long long>(N)));
+      csize[o] = n;
+      prun += (n + 31) & ~31;
+      orun += max(sz[j], 0);
     }
   }
 }
@@ -651,7 +678,7 @@ __global__ __launch_bounds__(256) void cl_gather_bf16_kernel(const uint16_t* __r
       const int r = c / (D / 8), c8 = c % (D / 8);
       const int tok = s0 + r < n ? ord[s0 + r] : -1;
       u32x4 kx = u32x4{0, 0, 0, 0}, vx = u32x4{0, 0, 0, 0};
-      if (tok >= 0) {
+      if (static_cast<unsigned>(tok) < static_cast<unsigned>(N)) {  // padding, or an invalid id: zeros
         const size_t g = (static_cast<size_t>(h) * N + tok) * D + c8 * 8;
         kx = *reinterpret_cast<const u32x4*>(k + g);
         vx = *reinterpret_cast<const u32x4*>(v + g);
@@ -696,7 +723,7 @@ __global__ __launch_bounds__(256) void cl_gather_f32_kernel(const float* __restr
     const int r = c / (D / 4), c4 = (c % (D / 4)) * 4;
     const int tok = r < n ? ord[r] : -1;
     f32x4 kx = f32x4{0.f, 0.f, 0.f, 0.f}, vx = f32x4{0.f, 0.f, 0.f, 0.f};
-    if (tok >= 0) {
+    if (static_cast<unsigned>(tok) < static_cast<unsigned>(N)) {
       const size_t g = (static_cast<size_t>(h) * N + tok) * D + c4;
       kx = *reinterpret_cast<const f32x4*>(k + g);
       vx = *reinterpret_cast<const f32x4*>(v + g);
@@ -769,7 +796,7 @@ __global__ __launch_bounds__(256) void cl_table_kernel(const int* __restrict__ c
 }
 
 struct ClAttnWs {
-  size_t kp_off, vp_off, pstart_off, ostart_off, tcount_off, table_off, total;
+  size_t kp_off, vp_off, pstart_off, ostart_off, csize_off, tcount_off, table_off, total;
   int Np, stride;
 };
 
@@ -786,7 +813,8 @@ ClAttnWs cl_attn_ws_layout(const Problem& p) {
   w.vp_off = kv;
   w.pstart_off = 2 * kv;
   w.ostart_off = w.pstart_off + al(4 * rows);
-  w.tcount_off = w.ostart_off + al(4 * rows);
+  w.csize_off = w.ostart_off + al(4 * rows);
+  w.tcount_off = w.csize_off + al(4 * rows);
   w.table_off = w.tcount_off + al(4 * rows);
   w.total = w.table_off + al(4 * rows * w.stride);
   return w;
@@ -801,23 +829,25 @@ hipError_t launch_cluster_attn_t(const Problem& p, const void* q, const void* k,
   char* base = static_cast<char*>(ws);
   int* pstart = reinterpret_cast<int*>(base + w.pstart_off);
   int* ostart = reinterpret_cast<int*>(base + w.ostart_off);
+  int* csize = reinterpret_cast<int*>(base + w.csize_off);
   int* tcount = reinterpret_cast<int*>(base + w.tcount_off);
   int* table = reinterpret_cast<int*>(base + w.table_off);
-  hipLaunchKernelGGL(cl_scan_kernel, dim3(p.heads), dim3(256), 0, stream, sizes, pstart, ostart, p.nb);
+  hipLaunchKernelGGL(cl_scan_kernel, dim3(p.heads), dim3(256), 0, stream, sizes, pstart, ostart, csize, p.nb,
+                     p.tokens);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.dtype == 0)
     hipLaunchKernelGGL((cl_gather_bf16_kernel<D>), dim3(p.nb, p.heads), dim3(256), 0, stream,
-                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), sizes, order, pstart,
+                       static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), csize, order, pstart,
                        ostart, reinterpret_cast<uint16_t*>(base + w.kp_off),
                        reinterpret_cast<uint16_t*>(base + w.vp_off), p.tokens, p.nb, w.Np);
   else
     hipLaunchKernelGGL((cl_gather_f32_kernel<D>), dim3(p.nb, p.heads), dim3(256), 0, stream,
-                       static_cast<const float*>(k), static_cast<const float*>(v), sizes, order, pstart, ostart,
+                       static_cast<const float*>(k), static_cast<const float*>(v), csize, order, pstart, ostart,
                        reinterpret_cast<float*>(base + w.kp_off), reinterpret_cast<float*>(base + w.vp_off),
                        p.tokens, p.nb, w.Np);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  hipLaunchKernelGGL(cl_table_kernel, dim3(p.nb, p.heads), dim3(256), 0, stream, counts, idx, sizes, pstart,
+  hipLaunchKernelGGL(cl_table_kernel, dim3(p.nb, p.heads), dim3(256), 0, stream, counts, idx, csize, pstart,
                      tcount, table, p.nb, w.stride);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.dtype == 0) {

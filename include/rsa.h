@@ -386,15 +386,18 @@ rsa_status rsa_score_clusters(const rsa_problem* p, const void* q, const float* 
  *   out[h,i,:] = sum_{t : labels[h,t] listed} softmax_t(scale * <q_i, k_t>) v_t,
  *
  * and lse as in rsa_block_sparse_attn (a row with no key: out 0, lse -inf).
- * sizes, order: as rsa_kmeans writes them.  q, k, v, out, lse as in
- * rsa_block_sparse_attn.  The call gathers k and v into cluster order (each
+ * sizes, order: as rsa_kmeans writes them.  Other values give meaningless
+ * results but stay inside the buffers: each size is clamped to [0, keys not
+ * yet taken by earlier clusters] and token ids outside [0, tokens) read as
+ * zero keys.  q, k, v, out, lse as in rsa_block_sparse_attn.  The call gathers k and v into cluster order (each
  * cluster padded with zeros to whole 32-key sub-tiles), turns each row's list
  * into a table of sub-tiles and runs the block-sparse attention kernel over
  * the tables (bf16: matrix cores as rsa_block_sparse_attn; fp32: fp32 FMA).
  * ws / ws_bytes: at least rsa_workspace_bytes(p, RSA_OP_CLUSTER_ATTN) bytes,
  * 256-byte aligned: padded k and v (bf16: v transposed), Np = tokens +
- * 31 * NB rounded up to 32 keys per head; cluster starts; per-row sub-tile
- * counts and tables of Np / 32 entries.
+ * 31 * NB rounded up to 32 keys per head; cluster starts (padded and in
+ * `order`) and the sizes as used; per-row sub-tile counts and tables of
+ * Np / 32 entries.
  * Non-finite values in q, k or v give undefined results.
  */
 rsa_status rsa_cluster_attn(const rsa_problem* p, const void* q, const void* k, const void* v, const int32_t* sizes,

@@ -83,7 +83,7 @@ def test_workspace_sizes():
     # cluster attention: k and v in the padded cluster layout, starts, sub-tile tables
     npad = -(-(75600 + 31 * 591) // 32) * 32
     rows = 40 * 591
-    assert B.workspace_bytes(p, B.OP_CLUSTER_ATTN) == (2 * al(2 * 40 * npad * 128) + 3 * al(4 * rows)
+    assert B.workspace_bytes(p, B.OP_CLUSTER_ATTN) == (2 * al(2 * 40 * npad * 128) + 4 * al(4 * rows)
                                                        + al(4 * rows * (npad // 32)))
     # query-pooled scorer: pooled q and k, then block maxima
     assert B.workspace_bytes(p, B.OP_POOLED) == 2 * al(4 * 40 * 591 * 128) + al(4 * 40 * 591)

@@ -272,3 +272,23 @@ def test_contiguous_clusters_equal_block_attention():
     assert (np.isneginf(la) == np.isneginf(lb)).all()
     live = np.isfinite(lb)
     assert np.abs(la[live] - lb[live]).max() <= 1e-5
+
+
+def test_cluster_attention_inconsistent_layout_stays_in_bounds():
+    """Sizes that overrun the keys and token ids out of range: the call
+    clamps them (results meaningless but finite, nothing written outside the
+    outputs)."""
+    c = case("bf16_d64_b64")
+    wl, p = c.wl, c.p
+    clustered(c)
+    rng = np.random.default_rng(460)
+    sizes = torch.from_numpy(rng.integers(-50, 4 * wl.tokens, (wl.heads, wl.nblocks)).astype(np.int32)).to(DEV)
+    order = torch.from_numpy(rng.integers(-wl.tokens, 2 * wl.tokens, (wl.heads, wl.tokens)).astype(np.int32)).to(DEV)
+    cnt = torch.full((wl.heads, wl.nblocks), wl.nblocks, dtype=torch.int32, device=DEV)
+    ix = torch.arange(wl.nblocks, dtype=torch.int32, device=DEV).repeat(wl.heads, wl.nblocks, 1).contiguous()
+    guard = torch.full((2, wl.heads, wl.tokens, wl.head_dim), 7.0, dtype=torch.bfloat16, device=DEV)
+    out = guard[0]
+    out, lse = R.cluster_attn(c.q, c.k, c.v, sizes, order, cnt, ix, p, out=out)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out.float()).all()
+    assert (guard[1] == 7.0).all()
