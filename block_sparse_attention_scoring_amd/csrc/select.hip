@@ -5,142 +5,157 @@
 // with a threshold per head (also HEART: Exploiting Head Heterogeneity in
 // Sparse Attention for Video Diffusion, Abstract).
 //
-// One workgroup per (head, query block) row.  The row's scores are packed
-// into 64-bit keys (inverted order-preserving score bits, key-block index),
-// so one ascending bitonic sort in LDS orders the blocks by score descending
-// and, for equal scores, by index ascending.  The sorted scores are summed in
-// fp64 with a block-wide scan; the first rank whose running mass reaches
-// p[h] fixes k*; the kept blocks are flagged and compacted in ascending
-// index order with an integer scan.  Nothing here depends on thread timing.
+// One wave per (head, query block) row, four rows per workgroup, no LDS and
+// no barriers.  The row's scores become 64-bit keys (inverted
+// order-preserving score bits, key-block index), so an ascending sort orders
+// the blocks by score descending and, for equal scores, by index ascending.
+// Each lane holds E consecutive keys of the padded row (MP = 64 E >= NB) in
+// registers; the bitonic network runs its strides below E inside the lane
+// and the others between lanes (shuffles).  The sorted scores are summed in
+// fp64 (in-lane, then a wave scan); the first rank whose running mass
+// reaches p[h] fixes k*, and the key at rank k* - 1 is the threshold: block
+// j is kept when its key is not above it, which the lanes test on the
+// unsorted row (E consecutive indices each) to write the mask and, with a
+// wave scan of the counts, the ascending list.  Nothing depends on timing.
 #include "common.h"
 #include "kernels.h"
 
 namespace rsa {
 namespace {
 
-constexpr int kSelThreads = 256;
+constexpr int kSelWaves = 4;  // rows per workgroup
 
 __device__ __forceinline__ uint32_t order_bits(float f) {
   const uint32_t u = __float_as_uint(f);
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);  // ascending in f
 }
+// inverse of ~order_bits: the score a key carries in its high word
+__device__ __forceinline__ float key_score(uint64_t key) {
+  const uint32_t o = ~static_cast<uint32_t>(key >> 32);
+  return __uint_as_float((o & 0x80000000u) ? (o & 0x7fffffffu) : ~o);
+}
 
 template <typename V>
-__device__ V block_exclusive_scan(V x, V* wave_tot, V& total) {
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ __forceinline__ V wave_exclusive_scan(V x, V& total) {
+  const int lane = threadIdx.x & 63;
   V incl = x;
 #pragma unroll
   for (int o = 1; o < 64; o <<= 1) {
     const V y = __shfl_up(incl, o);
     if (lane >= o) incl += y;
   }
-  if (lane == 63) wave_tot[wave] = incl;
-  __syncthreads();
-  V before = 0, all = 0;
-#pragma unroll
-  for (int w = 0; w < kSelThreads / kWave; ++w) {
-    if (w < wave) before += wave_tot[w];
-    all += wave_tot[w];
-  }
-  __syncthreads();
-  total = all;
-  return before + incl - x;
+  total = __shfl(incl, 63);
+  return incl - x;
 }
 
-__global__ __launch_bounds__(kSelThreads) void select_kernel(
+template <int E>
+__global__ __launch_bounds__(kSelWaves * kWave) void select_kernel(
     const float* __restrict__ scores, const float* __restrict__ top_p, int max_blocks,
     const uint8_t* __restrict__ head_active, uint8_t* __restrict__ mask,
-    int32_t* __restrict__ counts, int32_t* __restrict__ idx, int NB, int MP) {
-  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  uint64_t* keys = reinterpret_cast<uint64_t*>(smem);           // [MP]
-  float* sval = reinterpret_cast<float*>(keys + MP);             // [MP]
-  uint8_t* flag = reinterpret_cast<uint8_t*>(sval + MP);         // [MP]
-  __shared__ double dtot[kSelThreads / kWave];
-  __shared__ int itot[kSelThreads / kWave];
-  __shared__ int first_hit;
-
-  const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = tile / NB, I = tile - h * NB;
+    int32_t* __restrict__ counts, int32_t* __restrict__ idx, int H, int NB) {
+  constexpr int MP = E * kWave;
+  const int lane = threadIdx.x & 63;
+  const int row_id = blockIdx.x * kSelWaves + static_cast<int>(threadIdx.x >> 6);
+  if (row_id >= H * NB) return;  // whole waves leave together
+  const int h = row_id / NB;
   if (head_active != nullptr && head_active[h] == 0) return;
-  const int tid = threadIdx.x;
-  const float* srow = scores + (static_cast<size_t>(h) * NB + I) * NB;
+  const size_t row = static_cast<size_t>(row_id);
+  const float* srow = scores + row * NB;
 
-  for (int j = tid; j < MP; j += kSelThreads) {
-    if (j < NB) {
-      const float s = srow[j];
-      sval[j] = s;
-      keys[j] = (static_cast<uint64_t>(~order_bits(s)) << 32) | static_cast<uint32_t>(j);
-    } else {
-      keys[j] = ~0ull;
-    }
-    flag[j] = 0;
-  }
-  if (tid == 0) first_hit = 0x7fffffff;
-  __syncthreads();
-
-  // ascending bitonic sort of MP keys
+  // key of block j (padding past NB sorts last)
+  auto key_of = [&](int j) {
+    return j < NB ? (static_cast<uint64_t>(~order_bits(srow[j])) << 32) | static_cast<uint32_t>(j) : ~0ull;
+  };
+  // the row: lane holds indices lane*E .. lane*E + E - 1
+  uint64_t v[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) v[e] = key_of(lane * E + e);
+  // ascending bitonic sort of the MP keys
+#pragma unroll 1
   for (int size = 2; size <= MP; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int t = tid; t < MP / 2; t += kSelThreads) {
-        const int i = 2 * t - (t & (stride - 1));
-        const int j = i + stride;
-        const bool up = (i & size) == 0;
-        const uint64_t a = keys[i], b = keys[j];
-        if ((a > b) == up) {
-          keys[i] = b;
-          keys[j] = a;
+#pragma unroll 1
+    for (int stride = size >> 1; stride >= E; stride >>= 1) {
+      const int dl = stride / E;
+#pragma unroll
+      for (int e = 0; e < E; ++e) {
+        const uint64_t a = v[e], b = __shfl_xor(a, dl);
+        const int i = lane * E + e;
+        const bool lower = (i & stride) == 0, up = (i & size) == 0;
+        v[e] = (lower == up) ? (a < b ? a : b) : (a < b ? b : a);
+      }
+    }
+#pragma unroll
+    for (int st = E / 2; st >= 1; st >>= 1) {  // strides inside the lane (compile-time indices)
+      if (st < size) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+          if ((e & st) == 0) {
+            const uint64_t a = v[e], b = v[e + st];
+            const bool up = ((lane * E + e) & size) == 0;
+            if ((a > b) == up) {
+              v[e] = b;
+              v[e + st] = a;
+            }
+          }
         }
       }
-      __syncthreads();
     }
   }
 
-  // fp64 running mass over the sorted order: each thread owns E consecutive ranks
-  const int E = MP / kSelThreads;
-  const int r0 = tid * E;
-  double local = 0.0;
-  for (int e = 0; e < E; ++e) {
-    const int r = r0 + e;
-    if (r < NB) local += static_cast<double>(sval[static_cast<uint32_t>(keys[r])]);
-  }
-  double total;
-  double run = block_exclusive_scan<double>(local, dtot, total);
+  // k*: first rank whose fp64 running mass reaches p (ranks lane*E .. +E-1)
   const double p = static_cast<double>(top_p[h]);
-  int kstar;
-  if (p >= 1.0) {
-    kstar = NB;
-  } else {
+  int kstar = NB;
+  if (p < 1.0) {
+    double local = 0.0;
+#pragma unroll
+    for (int e = 0; e < E; ++e)
+      if (lane * E + e < NB) local += static_cast<double>(key_score(v[e]));
+    double total;
+    double run = wave_exclusive_scan<double>(local, total);
+    int hit = 0x7fffffff;
+#pragma unroll
     for (int e = 0; e < E; ++e) {
-      const int r = r0 + e;
-      if (r >= NB) break;
-      run += static_cast<double>(sval[static_cast<uint32_t>(keys[r])]);
-      if (run >= p) {
-        atomicMin(&first_hit, r);
-        break;
+      const int r = lane * E + e;
+      if (r < NB && hit == 0x7fffffff) {
+        run += static_cast<double>(key_score(v[e]));
+        if (run >= p) hit = r;
       }
     }
-    __syncthreads();
-    kstar = first_hit == 0x7fffffff ? NB : first_hit + 1;
+#pragma unroll
+    for (int o = 32; o >= 1; o >>= 1) hit = min(hit, __shfl_xor(hit, o));
+    if (hit != 0x7fffffff) kstar = hit + 1;
   }
   if (max_blocks > 0 && kstar > max_blocks) kstar = max_blocks;
+  // the key of rank kstar - 1: every key not above it is kept
+  const int rk = kstar - 1;
+  uint64_t thr = 0;
+#pragma unroll
+  for (int e = 0; e < E; ++e)
+    if (e == rk % E) thr = v[e];
+  thr = __shfl(thr, rk / E);
 
-  for (int r = tid; r < kstar; r += kSelThreads) flag[static_cast<uint32_t>(keys[r])] = 1;
-  __syncthreads();
-
-  uint8_t* mrow = mask + (static_cast<size_t>(h) * NB + I) * NB;
-  for (int j = tid; j < NB; j += kSelThreads) mrow[j] = flag[j];
-
-  // ascending compaction: thread owns E consecutive block indices
+  // mask and ascending list from the unsorted row (keys rebuilt from the
+  // scores: the row is still in cache; keys are unique, so exactly k* pass)
+  uint8_t* mrow = mask + row * NB;
   int cnt = 0;
-  for (int e = 0; e < E; ++e) cnt += (r0 + e < NB) ? flag[r0 + e] : 0;
-  int all;
-  int pos = block_exclusive_scan<int>(cnt, itot, all);
-  int32_t* irow = idx + (static_cast<size_t>(h) * NB + I) * NB;
+#pragma unroll
   for (int e = 0; e < E; ++e) {
-    const int j = r0 + e;
-    if (j < NB && flag[j]) irow[pos++] = j;
+    const int j = lane * E + e;
+    if (j < NB) {
+      const bool keep = key_of(j) <= thr;
+      mrow[j] = keep ? 1 : 0;
+      cnt += keep;
+    }
   }
-  if (tid == 0) counts[static_cast<size_t>(h) * NB + I] = kstar;
+  int all;
+  int pos = wave_exclusive_scan<int>(cnt, all);
+  int32_t* irow = idx + row * NB;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = lane * E + e;
+    if (j < NB && key_of(j) <= thr) irow[pos++] = j;
+  }
+  if (lane == 0) counts[row] = kstar;
 }
 
 // density[h] = sum_I counts[h, I] / NB^2, exact integer sum
@@ -165,11 +180,23 @@ __global__ __launch_bounds__(256) void density_kernel(const int32_t* __restrict_
 hipError_t launch_select(const Problem& p, const float* scores, const float* top_p,
                          int max_blocks, const uint8_t* head_active, uint8_t* mask,
                          int32_t* counts, int32_t* idx, float* density, hipStream_t stream) {
-  int MP = kSelThreads;
+  int MP = kWave;
   while (MP < p.nb) MP <<= 1;
-  const size_t lds = static_cast<size_t>(MP) * (sizeof(uint64_t) + sizeof(float) + 1);
-  hipLaunchKernelGGL(select_kernel, dim3(p.heads * p.nb), dim3(kSelThreads), lds, stream, scores,
-                     top_p, max_blocks, head_active, mask, counts, idx, p.nb, MP);
+  const int rows = p.heads * p.nb;
+  const dim3 grid((rows + kSelWaves - 1) / kSelWaves);
+  auto go = [&](auto kern) {
+    hipLaunchKernelGGL(kern, grid, dim3(kSelWaves * kWave), 0, stream, scores, top_p, max_blocks, head_active,
+                       mask, counts, idx, p.heads, p.nb);
+  };
+  switch (MP / kWave) {
+    case 1: go(select_kernel<1>); break;
+    case 2: go(select_kernel<2>); break;
+    case 4: go(select_kernel<4>); break;
+    case 8: go(select_kernel<8>); break;
+    case 16: go(select_kernel<16>); break;
+    case 32: go(select_kernel<32>); break;
+    default: go(select_kernel<64>); break;  // NB <= 4096
+  }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || density == nullptr) return e;
   hipLaunchKernelGGL(density_kernel, dim3(p.heads), dim3(256), 0, stream, counts, density, p.nb);
