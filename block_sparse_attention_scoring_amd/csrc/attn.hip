@@ -94,6 +94,67 @@ __global__ __launch_bounds__(256) void canon_kernel(const int* __restrict__ coun
   if (tid == 0) ccount[row] = base;
 }
 
+// Pair lists for 64-token blocks.  One workgroup per (pair P, head h): the
+// lists of query blocks 2P and 2P+1, read as sets like canon_kernel reads
+// them, are marked in two LDS byte maps; the union is compacted in
+// ascending order, each entry J | (bits << 16) where bit 0 / bit 1 says
+// that block 2P / 2P+1 lists J.  With `complement` set each row's blocks not
+// listed are taken instead.  Heads with head_active[h] == 0 are skipped.
+__global__ __launch_bounds__(256) void pair_canon_kernel(const int* __restrict__ counts,
+                                                         const int* __restrict__ block_idx,
+                                                         const uint8_t* __restrict__ head_active,
+                                                         int complement, int* __restrict__ ccount,
+                                                         int* __restrict__ clist, int NB) {
+  __shared__ uint8_t mark0[kMaxNB];
+  __shared__ uint8_t mark1[kMaxNB];
+  __shared__ int wsum[4];
+  const int P = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  if (head_active != nullptr && head_active[h] == 0) return;
+  const int lane = tid & 63, wave = tid >> 6;
+  for (int e = tid; e < NB; e += 256) {
+    mark0[e] = 0;
+    mark1[e] = 0;
+  }
+  __syncthreads();
+  const int nrows = min(2, NB - 2 * P);  // the last pair may hold one block
+  for (int q = 0; q < nrows; ++q) {
+    const size_t row = static_cast<size_t>(h) * NB + 2 * P + q;
+    uint8_t* mk = q == 0 ? mark0 : mark1;
+    const int c = min(max(counts[row], 0), NB);
+    for (int t = tid; t < c; t += 256) {
+      const int j = block_idx[row * NB + t];
+      if (static_cast<unsigned>(j) < static_cast<unsigned>(NB)) mk[j] = 1;
+    }
+  }
+  __syncthreads();
+  const int rows_bits = nrows == 2 ? 3 : 1;
+  int* out = clist + (static_cast<size_t>(h) * NB + P) * NB;
+  int base = 0;
+  for (int r0 = 0; r0 < NB; r0 += 256) {
+    const int e = r0 + tid;
+    int bits = 0;
+    if (e < NB) {
+      bits = mark0[e] | (mark1[e] << 1);
+      if (complement) bits = rows_bits & ~bits;
+    }
+    const bool f = bits != 0;
+    const uint64_t bal = __ballot(f);
+    const int pre = __builtin_popcountll(bal & ((1ull << lane) - 1));
+    if (lane == 0) wsum[wave] = __builtin_popcountll(bal);
+    __syncthreads();
+    int off = base, tot = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      off += w < wave ? wsum[w] : 0;
+      tot += wsum[w];
+    }
+    if (f) out[off + pre] = e | (bits << 16);
+    base += tot;
+    __syncthreads();
+  }
+  if (tid == 0) ccount[static_cast<size_t>(h) * NB + P] = base;
+}
+
 // Work of one workgroup: B/32 waves (32 query rows each) against key
 // sub-tiles of KS keys; NBUF LDS buffers per operand.
 template <int D, int B, int KS, int NBUF>
@@ -161,7 +222,13 @@ __global__ __launch_bounds__(256) void vt_kernel(const uint16_t* __restrict__ v,
 // key blocks): entry e is a sub-tile at key e & ~31 of the padded cluster
 // layout holding (e & 31) + 1 real keys; K has Nk rows and V^T Nv columns per
 // head.  Every sub-tile may be partial, so each step applies its mask.
-template <int D, int B, int KS, int NBUF, bool kTable = false>
+//
+// BQ < B (pair mode, BQ = B/2 = 64): the workgroup serves query blocks 2P and
+// 2P+1 of BQ tokens (waves 0-1 and 2-3) over the union of their lists
+// (pair_canon_kernel); each wave skips the sub-tiles its own block did not
+// select.  Two workgroups share a CU, so the two waves of a SIMD still come
+// from different workgroups.
+template <int D, int B, int KS, int NBUF, bool kTable = false, int BQ = B>
 __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const int* __restrict__ ccount,
@@ -171,6 +238,9 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
   using S = AttnShape<D, B, KS, NBUF>;
   static_assert(NBUF >= 3 && NBUF <= 4, "ring of 3 or 4 LDS slots");
   static_assert(!kTable || KS == 32, "table entries are 32-key sub-tiles");
+  constexpr bool kPair = BQ != B;
+  static_assert(!kPair || (2 * BQ == B && !kTable && BQ % KS == 0), "pair mode: two blocks of B/2 tokens");
+  constexpr int kSubQ = BQ / KS;  // sub-tiles per listed key block
   // Ring slots: K sub-tile at [0, kTile), V^T sub-tile after it.  Separate
   // arrays, addressed with compile-time slot numbers, let the compiler see
   // that the slot being filled is not the one being read, so it does not
@@ -183,10 +253,11 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
   // Head-synchronous schedule: workgroup ids go round-robin over the 8 XCDs;
   // XCD x takes the x-th contiguous eighth of the query blocks of one head
   // after another, so all XCDs share one head's K/V at a time.
-  const int per_xcd = (NB + 7) / 8;
+  const int units = kPair ? (NB + 1) / 2 : NB;  // query blocks, or pairs of them
+  const int per_xcd = (units + 7) / 8;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
   const int h = slot / per_xcd, I = xcd * per_xcd + slot % per_xcd;
-  if (h >= H || I >= NB) return;
+  if (h >= H || I >= units) return;
   if (head_active != nullptr && head_active[h] == 0) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
@@ -194,7 +265,8 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
   const int hl = lane >> 5, col = lane & 31;
   const size_t head_off = static_cast<size_t>(h) * N * D;
   const size_t np = static_cast<size_t>(Nv);
-  const int qrow = I * B + wave * 32 + col;
+  const int qrow = kPair ? (2 * I + (wave >> 1)) * BQ + (wave & 1) * 32 + col : I * B + wave * 32 + col;
+  const int mbit = kPair ? 1 << (wave >> 1) : 0;  // this wave's bit in a pair entry
 
   bf16x8 qf[S::kKSD];
   {
@@ -208,7 +280,7 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
   }
 
   const int cnt = ccount[h * NB + I];
-  const int total = kTable ? cnt : cnt * S::kSub;  // sub-tiles to visit
+  const int total = kTable ? cnt : cnt * kSubQ;  // sub-tiles to visit
   const int* list = clist + (static_cast<size_t>(h) * NB + I) * lstride;
   const uint16_t* kh = k + static_cast<size_t>(h) * Nk * D;
   const uint16_t* vth = vt + static_cast<size_t>(h) * D * np;
@@ -216,8 +288,10 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
   // first key of sub-tile u
   auto sub_base = [&](int u) {
     if constexpr (kTable) return list[u] & ~31;
-    else return list[u / S::kSub] * B + (u % S::kSub) * KS;
+    else return (list[u / kSubQ] & 0xffff) * BQ + (u % kSubQ) * KS;
   };
+  // whether this wave's query block selected sub-tile u (pair mode)
+  auto member = [&](int u) { return !kPair || ((list[u / kSubQ] >> 16) & mbit) != 0; };
 
   // Tiles are fetched with buffer loads straight into LDS.  Each lane's byte
   // offset inside a sub-tile is fixed for the whole loop, so only scalar
@@ -371,34 +445,60 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
   // ascending, so only its last entry can be the ragged block NB-1
   int total_full = total;
   if (!kTable && total > 0) {
-    const int last = list[cnt - 1];
-    if (last == NB - 1) total_full = total - S::kSub + min(S::kSub, (N - last * B) / KS);
+    const int last = list[cnt - 1] & 0xffff;
+    if (last == NB - 1) total_full = total - kSubQ + min(kSubQ, (N - last * BQ) / KS);
   }
   int next = min(NBUF - 2, total);  // first sub-tile not yet requested
   for (int i = 0; i < NBUF - 2 && i < total; ++i) issue(i, ring(i));
   int j = 0;
-  bool pending = false;  // sprev holds sub-tile j-1, not yet in O
+  bool pending = false;  // sprev holds sub-tile j-1, not yet in O (if pvalid)
+  bool pvalid = true;
   if (total_full >= NBUF + 1 && total >= 2 * NBUF - 2) {
     wait_vm<(NBUF - 3) * kPer>();
     barrier_lds();
     issue(NBUF - 2, ring(NBUF - 2));
-    qk(slot0, sprev);
-    if constexpr (kTable) mask_tail(0, sprev);
-    mprev = rowmax(sprev);
+    pvalid = member(0);  // sprev holds a sub-tile this wave selected
+    if (pvalid) {
+      qk(slot0, sprev);
+      if constexpr (kTable) mask_tail(0, sprev);
+      mprev = rowmax(sprev);
+    }
     j = 1;
     pending = true;
     auto step = [&](const uint16_t* kslot, const uint16_t* vslot, uint16_t* fill, int jj) {
-      rescale(mprev);
-      wait_vm<(NBUF - 3) * kPer>();
-      barrier_lds();
-      issue(jj + NBUF - 2, fill);
-      f32x16 scur[S::kKT];
-      qk(kslot, scur);
-      pv(sprev, vslot);
+      if constexpr (!kPair) {
+        rescale(mprev);
+        wait_vm<(NBUF - 3) * kPer>();
+        barrier_lds();
+        issue(jj + NBUF - 2, fill);
+        f32x16 scur[S::kKT];
+        qk(kslot, scur);
+        pv(sprev, vslot);
 #pragma unroll
-      for (int t = 0; t < S::kKT; ++t) sprev[t] = scur[t];
-      if constexpr (kTable) mask_tail(jj, sprev);
-      mprev = rowmax(sprev);
+        for (int t = 0; t < S::kKT; ++t) sprev[t] = scur[t];
+        if constexpr (kTable) mask_tail(jj, sprev);
+        mprev = rowmax(sprev);
+      } else {
+        const bool mc = member(jj);
+        if (pvalid) rescale(mprev);
+        wait_vm<(NBUF - 3) * kPer>();
+        barrier_lds();
+        issue(jj + NBUF - 2, fill);
+        if (mc && pvalid) {
+          f32x16 scur[S::kKT];
+          qk(kslot, scur);
+          pv(sprev, vslot);
+#pragma unroll
+          for (int t = 0; t < S::kKT; ++t) sprev[t] = scur[t];
+          mprev = rowmax(sprev);
+        } else if (mc) {
+          qk(kslot, sprev);
+          mprev = rowmax(sprev);
+        } else if (pvalid) {
+          pv(sprev, vslot);
+        }
+        pvalid = mc;
+      }
     };
     // groups of NBUF steps starting at j = 1 mod NBUF: compile-time slots
     while (j + NBUF - 1 < total_full && j + 2 * NBUF - 3 < total) {
@@ -410,7 +510,7 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
     }
     next = j + NBUF - 2;
   }
-  if (pending) {  // finish sub-tile j-1
+  if (pending && pvalid) {  // finish sub-tile j-1
     rescale(mprev);
     pv(sprev, ring((j - 1) % NBUF));
   }
@@ -419,11 +519,13 @@ __global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
     wait_vm<0>();
     barrier_lds();
     for (; next < total && next <= j + NBUF - 1; ++next) issue(next, ring(next % NBUF));
-    f32x16 sc[S::kKT];
-    qk(ring(j % NBUF), sc);
-    mask_tail(j, sc);
-    rescale(rowmax(sc));
-    pv(sc, ring(j % NBUF));
+    if (member(j)) {
+      f32x16 sc[S::kKT];
+      qk(ring(j % NBUF), sc);
+      mask_tail(j, sc);
+      rescale(rowmax(sc));
+      pv(sc, ring(j % NBUF));
+    }
   }
 
   const float l_run = (l_part[0] + l_part[1]) + (l_part[2] + l_part[3]);
@@ -549,23 +651,31 @@ hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const v
   char* base = static_cast<char*>(ws);
   int* ccount = reinterpret_cast<int*>(base + w.ccount_off);
   int* clist = reinterpret_cast<int*>(base + w.clist_off);
-  hipLaunchKernelGGL(canon_kernel, dim3(p.nb, p.heads), dim3(256), 0, stream, counts, idx, head_active,
-                     complement, ccount, clist, p.nb);
+  // 64-token blocks on the matrix cores: pairs of query blocks per workgroup
+  constexpr bool kPairs = B == 64;
+  if (p.dtype == 0 && kPairs)
+    hipLaunchKernelGGL(pair_canon_kernel, dim3((p.nb + 1) / 2, p.heads), dim3(256), 0, stream, counts, idx,
+                       head_active, complement, ccount, clist, p.nb);
+  else
+    hipLaunchKernelGGL(canon_kernel, dim3(p.nb, p.heads), dim3(256), 0, stream, counts, idx, head_active,
+                       complement, ccount, clist, p.nb);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.dtype == 0) {
     // 64 KB of LDS per 128-row workgroup (two per CU): a ring of four 32-key
-    // sub-tiles; 48 KB per 64-row workgroup: three 32-key slots
-    constexpr int kKs = RSA_ATTN_KS, kNbuf = B == 128 ? RSA_ATTN_NBUF : 3;
-    using S = AttnShape<D, B, kKs, kNbuf>;
+    // sub-tiles
+    constexpr int kKs = RSA_ATTN_KS, kNbuf = RSA_ATTN_NBUF;
+    constexpr int kRows = 128;  // query rows per workgroup (a block, or a pair of 64-token blocks)
+    using S = AttnShape<D, kRows, kKs, kNbuf>;
     uint16_t* vt = reinterpret_cast<uint16_t*>(base);
     hipLaunchKernelGGL((vt_kernel<D, B>), dim3(p.nb, p.heads), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(v), head_active, vt, p.tokens, p.nb);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int grid = 8 * ((p.nb + 7) / 8) * p.heads;
-    hipLaunchKernelGGL((attn_bf16_kernel<D, B, kKs, kNbuf>), dim3(grid), dim3(S::kThreads), 0, stream,
-                       static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt, ccount,
+    const int units = kPairs ? (p.nb + 1) / 2 : p.nb;
+    const int grid = 8 * ((units + 7) / 8) * p.heads;
+    hipLaunchKernelGGL((attn_bf16_kernel<D, kRows, kKs, kNbuf, false, B>), dim3(grid), dim3(S::kThreads), 0,
+                       stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt, ccount,
                        clist, head_active, static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2,
                        p.tokens, p.nb * B, p.nb);
   } else {
