@@ -225,8 +225,9 @@ rsa_status rsa_mask_drift(const rsa_problem* p, const void* q, const void* k,
  *   aligned, each part rounded up to 256 bytes: (bf16 only) v re-laid out
  *   key-major for the matrix cores, heads * head_dim * NB * block * 2 bytes;
  *   then every row's list in canonical form (ascending, no repeats, no
- *   invalid entries): counts, heads * NB * 4 bytes, and lists,
- *   heads * NB * NB * 4 bytes.
+ *   invalid entries; bf16 with block 64: the union of query blocks 2P and
+ *   2P+1 per pair, with membership bits): counts, heads * NB * 4 bytes, and
+ *   lists, heads * NB * NB * 4 bytes.
  * Non-finite values in q, k or v give undefined results.
  */
 rsa_status rsa_block_sparse_attn(const rsa_problem* p, const void* q, const void* k,
