@@ -26,13 +26,13 @@
 namespace rsa {
 namespace {
 
-// Key sub-tile width and LDS ring depth of the 128-row bf16 kernel (kept
-// overridable at build time for tuning sweeps).
+// Key sub-tile width of the 128-row bf16 kernel and the LDS ring depth of
+// its single-block mode (kept overridable at build time for tuning sweeps).
 #ifndef RSA_ATTN_KS
 #define RSA_ATTN_KS 32
 #endif
 #ifndef RSA_ATTN_NBUF
-#define RSA_ATTN_NBUF 4
+#define RSA_ATTN_NBUF 3
 #endif
 
 // Position of `key` inside its 16-key group of V^T: the S^T result layout
@@ -215,8 +215,11 @@ __global__ __launch_bounds__(256) void vt_kernel(const uint16_t* __restrict__ v,
 // 16 bytes per lane, each lane fetching the chunk that belongs at its slot of
 // the swizzled layout).  Each wave software-pipelines its own work: the
 // matrix products for sub-tile j run next to the exponentials of sub-tile
-// j-1.  Two workgroups share a CU, so the two waves on every SIMD also
-// overlap each other's vector and matrix work.
+// j-1.  Several workgroups share a CU, so the waves on every SIMD also
+// overlap each other's vector and matrix work: with a ring of three slots
+// (48 KB of LDS at D = 128) three workgroups fit, and the register budget
+// is capped to match (168 VGPRs, three waves per SIMD); with four slots
+// (64 KB) two fit, at up to 256 VGPRs.
 //
 // kTable: the row lists 32-key sub-tiles instead of key blocks (clusters as
 // key blocks): entry e is a sub-tile at key e & ~31 of the padded cluster
@@ -226,10 +229,9 @@ __global__ __launch_bounds__(256) void vt_kernel(const uint16_t* __restrict__ v,
 // BQ < B (pair mode, BQ = B/2 = 64): the workgroup serves query blocks 2P and
 // 2P+1 of BQ tokens (waves 0-1 and 2-3) over the union of their lists
 // (pair_canon_kernel); each wave skips the sub-tiles its own block did not
-// select.  Two workgroups share a CU, so the two waves of a SIMD still come
-// from different workgroups.
+// select.  Each SIMD's waves still come from different workgroups.
 template <int D, int B, int KS, int NBUF, bool kTable = false, int BQ = B>
-__global__ __launch_bounds__(2 * B, 2) void attn_bf16_kernel(
+__global__ __launch_bounds__(2 * B, NBUF == 3 ? 3 : 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const int* __restrict__ ccount,
     const int* __restrict__ clist, const uint8_t* __restrict__ head_active,
@@ -662,9 +664,10 @@ hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const v
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.dtype == 0) {
-    // 64 KB of LDS per 128-row workgroup (two per CU): a ring of four 32-key
-    // sub-tiles
-    constexpr int kKs = RSA_ATTN_KS, kNbuf = RSA_ATTN_NBUF;
+    // Single blocks: a ring of three 32-key sub-tiles, three workgroups per
+    // CU.  Pairs keep four slots and two workgroups per CU: their
+    // membership masks do not fit the three-wave register budget.
+    constexpr int kKs = RSA_ATTN_KS, kNbuf = kPairs ? 4 : RSA_ATTN_NBUF;
     constexpr int kRows = 128;  // query rows per workgroup (a block, or a pair of 64-token blocks)
     using S = AttnShape<D, kRows, kKs, kNbuf>;
     uint16_t* vt = reinterpret_cast<uint16_t*>(base);
@@ -961,7 +964,9 @@ hipError_t launch_cluster_attn_t(const Problem& p, const void* q, const void* k,
                      tcount, table, p.nb, w.stride);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.dtype == 0) {
-    constexpr int kNbuf = B == 128 ? RSA_ATTN_NBUF : 3;
+    // four slots for 128-token rows: the sub-tile masks do not fit the
+    // three-wave register budget
+    constexpr int kNbuf = B == 128 ? 4 : 3;
     using S = AttnShape<D, B, 32, kNbuf>;
     const int grid = 8 * ((p.nb + 7) / 8) * p.heads;
     hipLaunchKernelGGL((attn_bf16_kernel<D, B, 32, kNbuf, true>), dim3(grid), dim3(S::kThreads), 0, stream,
