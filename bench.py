@@ -571,7 +571,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
             "traffic": profiled_traffic(),
-            "kernel": "attn_bf16_kernel<128,128,32,4>",
+            "kernel": "attn_bf16_kernel<128,128,32,3>",
             # HIP events bracket the whole library call, which also runs the
             # V^T relayout and list canonicalisation kernels (about 1%)
             "timed": "rsa_block_sparse_attn call",
