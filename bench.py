@@ -16,7 +16,9 @@ pairs) / step time.  The attention call alone (ms per call, effective
 TFLOP/s) and every other kernel's time are reported beside it, each averaged
 over the timed steps with HIP events recorded on the stream the library
 launches on.  The oracle (fp64 NumPy) is timed on a bounded sample on the
-host cores as a CPU baseline.
+host cores as a CPU baseline, and the vendor bf16 GEMM (hipBLASLt through
+torch.matmul) is timed after the steps as the matrix-core rate this GPU
+sustains under load (roofline.vendor_gemm).
 """
 from __future__ import annotations
 
