@@ -155,6 +155,66 @@ __global__ __launch_bounds__(256) void pair_canon_kernel(const int* __restrict__
   if (tid == 0) ccount[static_cast<size_t>(h) * NB + P] = base;
 }
 
+// Dispatch order of one head's units (query blocks, or pairs of them) over
+// the 8 XCDs.  Units are ranked by canonical list length, longest first
+// (counting sort; units of equal length in any order), and dealt in a snake
+// over the XCDs: ranks 0-7 to XCDs 0..7, ranks 8-15 to XCDs 7..0, and so on.
+// Every XCD gets an eighth of the head's work, longest walks first, so the
+// XCDs finish together and the grid's tail holds only short walks.
+// perm[h, x, r] is the unit XCD x runs r-th for head h, or -1 where the
+// eighth is one short.  One workgroup per head; skipped for inactive heads.
+__global__ __launch_bounds__(256) void order_kernel(const int* __restrict__ ccount,
+                                                    const uint8_t* __restrict__ head_active,
+                                                    int* __restrict__ perm, int NB, int units, int per_xcd) {
+  constexpr int kPer = (kMaxNB + 1 + 255) / 256;  // lengths 0..NB, NB <= kMaxNB
+  __shared__ int start[kMaxNB + 1];  // per length: first rank, then next free rank
+  __shared__ int sorted[kMaxNB];     // unit of each rank
+  __shared__ int part[256];
+  const int h = blockIdx.x, tid = threadIdx.x;
+  if (head_active != nullptr && head_active[h] == 0) return;
+  const int* cnt = ccount + static_cast<size_t>(h) * NB;
+  for (int i = tid; i <= NB; i += 256) start[i] = 0;
+  __syncthreads();
+  for (int u = tid; u < units; u += 256) atomicAdd(&start[min(max(cnt[u], 0), NB)], 1);
+  __syncthreads();
+  // exclusive scan over lengths NB, NB-1, ..., 0 (longest first): thread t
+  // takes positions [t*kPer, (t+1)*kPer) of that descending order
+  int local = 0;
+  for (int e = 0; e < kPer; ++e) {
+    const int len = NB - (tid * kPer + e);
+    if (len >= 0) local += start[len];
+  }
+  part[tid] = local;
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int i = 0; i < 256; ++i) {
+      const int v = part[i];
+      part[i] = run;
+      run += v;
+    }
+  }
+  __syncthreads();
+  int run = part[tid];
+  for (int e = 0; e < kPer; ++e) {
+    const int len = NB - (tid * kPer + e);
+    if (len >= 0) {
+      const int c = start[len];
+      start[len] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  for (int u = tid; u < units; u += 256) sorted[atomicAdd(&start[min(max(cnt[u], 0), NB)], 1)] = u;
+  __syncthreads();
+  int* ph = perm + static_cast<size_t>(h) * 8 * per_xcd;
+  for (int pos = tid; pos < 8 * per_xcd; pos += 256) {
+    const int x = pos / per_xcd, row = pos % per_xcd;
+    const int r = row * 8 + ((row & 1) ? 7 - x : x);
+    ph[pos] = r < units ? sorted[r] : -1;
+  }
+}
+
 // Work of one workgroup: B/32 waves (32 query rows each) against key
 // sub-tiles of KS keys; NBUF LDS buffers per operand.
 template <int D, int B, int KS, int NBUF>
@@ -234,7 +294,7 @@ template <int D, int B, int KS, int NBUF, bool kTable = false, int BQ = B>
 __global__ __launch_bounds__(2 * B, NBUF == 3 ? 3 : 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const int* __restrict__ ccount,
-    const int* __restrict__ clist, const uint8_t* __restrict__ head_active,
+    const int* __restrict__ clist, const uint8_t* __restrict__ head_active, const int* __restrict__ perm,
     uint16_t* __restrict__ out, float* __restrict__ lse, int H, int N, int NB, float scale_log2,
     int Nk, int Nv, int lstride) {
   using S = AttnShape<D, B, KS, NBUF>;
@@ -253,14 +313,19 @@ __global__ __launch_bounds__(2 * B, NBUF == 3 ? 3 : 2) void attn_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t slot3[NBUF > 3 ? 2 * S::kTile : 8];
 
   // Head-synchronous schedule: workgroup ids go round-robin over the 8 XCDs;
-  // XCD x takes the x-th contiguous eighth of the query blocks of one head
-  // after another, so all XCDs share one head's K/V at a time.
+  // XCD x takes an eighth of the units of one head after another, so all
+  // XCDs share one head's K/V at a time.  With perm (order_kernel) the
+  // eighths are balanced by list length, longest walks first; without it
+  // XCD x takes the x-th contiguous eighth in order.
   const int units = kPair ? (NB + 1) / 2 : NB;  // query blocks, or pairs of them
   const int per_xcd = (units + 7) / 8;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int h = slot / per_xcd, I = xcd * per_xcd + slot % per_xcd;
-  if (h >= H || I >= units) return;
+  const int h = slot / per_xcd;
+  if (h >= H) return;
   if (head_active != nullptr && head_active[h] == 0) return;
+  const int pos = xcd * per_xcd + slot % per_xcd;
+  const int I = perm != nullptr ? perm[static_cast<size_t>(h) * 8 * per_xcd + pos] : pos;
+  if (I < 0 || I >= units) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS addresses stay scalar
@@ -631,7 +696,7 @@ __global__ __launch_bounds__(B) void attn_f32_kernel(
 // Attention workspace: [V^T (bf16 only)][canonical counts][canonical lists],
 // each part 256-byte aligned.
 struct AttnWs {
-  size_t ccount_off, clist_off, total;
+  size_t ccount_off, clist_off, perm_off, total;
 };
 
 AttnWs attn_ws_layout(const Problem& p) {
@@ -640,7 +705,9 @@ AttnWs attn_ws_layout(const Problem& p) {
   AttnWs w;
   w.ccount_off = p.dtype == 0 ? al(sizeof(uint16_t) * p.heads * p.head_dim * static_cast<size_t>(p.nb) * p.block) : 0;
   w.clist_off = w.ccount_off + al(sizeof(int) * rows);
-  w.total = w.clist_off + al(sizeof(int) * rows * p.nb);
+  w.perm_off = w.clist_off + al(sizeof(int) * rows * p.nb);
+  // dispatch order (bf16 path): per head 8 eighths of ceil(NB / 8) units
+  w.total = w.perm_off + (p.dtype == 0 ? al(sizeof(int) * p.heads * 8 * static_cast<size_t>((p.nb + 7) / 8)) : 0);
   return w;
 }
 
@@ -676,10 +743,16 @@ hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const v
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int units = kPairs ? (p.nb + 1) / 2 : p.nb;
-    const int grid = 8 * ((units + 7) / 8) * p.heads;
+    const int per_xcd = (units + 7) / 8;
+    int* perm = reinterpret_cast<int*>(base + w.perm_off);
+    hipLaunchKernelGGL(order_kernel, dim3(p.heads), dim3(256), 0, stream, ccount, head_active, perm, p.nb,
+                       units, per_xcd);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    const int grid = 8 * per_xcd * p.heads;
     hipLaunchKernelGGL((attn_bf16_kernel<D, kRows, kKs, kNbuf, false, B>), dim3(grid), dim3(S::kThreads), 0,
                        stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt, ccount,
-                       clist, head_active, static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2,
+                       clist, head_active, perm, static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2,
                        p.tokens, p.nb * B, p.nb);
   } else {
     hipLaunchKernelGGL((attn_f32_kernel<D, B>), dim3(p.heads * p.nb), dim3(B), 0, stream,
@@ -971,7 +1044,7 @@ hipError_t launch_cluster_attn_t(const Problem& p, const void* q, const void* k,
     const int grid = 8 * ((p.nb + 7) / 8) * p.heads;
     hipLaunchKernelGGL((attn_bf16_kernel<D, B, 32, kNbuf, true>), dim3(grid), dim3(S::kThreads), 0, stream,
                        static_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(base + w.kp_off),
-                       reinterpret_cast<const uint16_t*>(base + w.vp_off), tcount, table, nullptr,
+                       reinterpret_cast<const uint16_t*>(base + w.vp_off), tcount, table, nullptr, nullptr,
                        static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2, w.Np, w.Np, w.stride);
   } else {
     hipLaunchKernelGGL((attn_f32_kernel<D, B, true>), dim3(p.heads * p.nb), dim3(B), 0, stream,

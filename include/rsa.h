@@ -227,7 +227,8 @@ rsa_status rsa_mask_drift(const rsa_problem* p, const void* q, const void* k,
  *   then every row's list in canonical form (ascending, no repeats, no
  *   invalid entries; bf16 with block 64: the union of query blocks 2P and
  *   2P+1 per pair, with membership bits): counts, heads * NB * 4 bytes, and
- *   lists, heads * NB * NB * 4 bytes.
+ *   lists, heads * NB * NB * 4 bytes; then (bf16 only) the workgroup
+ *   dispatch order, heads * 8 * ceil(NB / 8) * 4 bytes.
  * Non-finite values in q, k or v give undefined results.
  */
 rsa_status rsa_block_sparse_attn(const rsa_problem* p, const void* q, const void* k,

@@ -66,9 +66,10 @@ def test_workspace_sizes():
     assert B.workspace_bytes(p, B.OP_DRIFT) == 8 * 2 * 64 * 40
     assert B.workspace_bytes(p, B.OP_SELECT) == 0
     # attention: v re-laid out key-major (bf16), then the canonical list
-    # counts and lists of every row
+    # counts and lists of every row, then (bf16) the dispatch order
     lists = al(4 * 40 * 591) + al(4 * 40 * 591 * 591)
-    assert B.workspace_bytes(p, B.OP_ATTN) == al(2 * 40 * 128 * 591 * 128) + lists
+    order = al(4 * 40 * 8 * 74)
+    assert B.workspace_bytes(p, B.OP_ATTN) == al(2 * 40 * 128 * 591 * 128) + lists + order
     assert B.workspace_bytes(prob(heads=40, grid=(21, 45, 80), b=128, dtype=1), B.OP_ATTN) == lists
     # Gram matrix: one D x D fp32 partial per 2048 tokens (bf16 only)
     assert B.workspace_bytes(p, B.OP_GRAM) == al(4 * 40 * 37 * 128 * 128)
