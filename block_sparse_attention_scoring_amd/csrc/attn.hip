@@ -156,8 +156,9 @@ __global__ __launch_bounds__(256) void pair_canon_kernel(const int* __restrict__
 }
 
 // Dispatch order of one head's units (query blocks, or pairs of them) over
-// the 8 XCDs.  Units are ranked by canonical list length, longest first
-// (counting sort; units of equal length in any order), and dealt in a snake
+// the 8 XCDs.  Units are ranked by list length (ccount, clamped to
+// [0, maxlen], maxlen <= kMaxNB), longest first (counting sort; units of
+// equal length in any order), and dealt in a snake
 // over the XCDs: ranks 0-7 to XCDs 0..7, ranks 8-15 to XCDs 7..0, and so on.
 // Every XCD gets an eighth of the head's work, longest walks first, so the
 // XCDs finish together and the grid's tail holds only short walks.
@@ -165,23 +166,24 @@ __global__ __launch_bounds__(256) void pair_canon_kernel(const int* __restrict__
 // eighth is one short.  One workgroup per head; skipped for inactive heads.
 __global__ __launch_bounds__(256) void order_kernel(const int* __restrict__ ccount,
                                                     const uint8_t* __restrict__ head_active,
-                                                    int* __restrict__ perm, int NB, int units, int per_xcd) {
-  constexpr int kPer = (kMaxNB + 1 + 255) / 256;  // lengths 0..NB, NB <= kMaxNB
+                                                    int* __restrict__ perm, int NB, int units, int per_xcd,
+                                                    int maxlen) {
+  constexpr int kPer = (kMaxNB + 1 + 255) / 256;  // lengths 0..maxlen
   __shared__ int start[kMaxNB + 1];  // per length: first rank, then next free rank
   __shared__ int sorted[kMaxNB];     // unit of each rank
   __shared__ int part[256];
   const int h = blockIdx.x, tid = threadIdx.x;
   if (head_active != nullptr && head_active[h] == 0) return;
   const int* cnt = ccount + static_cast<size_t>(h) * NB;
-  for (int i = tid; i <= NB; i += 256) start[i] = 0;
+  for (int i = tid; i <= maxlen; i += 256) start[i] = 0;
   __syncthreads();
-  for (int u = tid; u < units; u += 256) atomicAdd(&start[min(max(cnt[u], 0), NB)], 1);
+  for (int u = tid; u < units; u += 256) atomicAdd(&start[min(max(cnt[u], 0), maxlen)], 1);
   __syncthreads();
-  // exclusive scan over lengths NB, NB-1, ..., 0 (longest first): thread t
+  // exclusive scan over lengths maxlen, ..., 0 (longest first): thread t
   // takes positions [t*kPer, (t+1)*kPer) of that descending order
   int local = 0;
   for (int e = 0; e < kPer; ++e) {
-    const int len = NB - (tid * kPer + e);
+    const int len = maxlen - (tid * kPer + e);
     if (len >= 0) local += start[len];
   }
   part[tid] = local;
@@ -197,7 +199,7 @@ __global__ __launch_bounds__(256) void order_kernel(const int* __restrict__ ccou
   __syncthreads();
   int run = part[tid];
   for (int e = 0; e < kPer; ++e) {
-    const int len = NB - (tid * kPer + e);
+    const int len = maxlen - (tid * kPer + e);
     if (len >= 0) {
       const int c = start[len];
       start[len] = run;
@@ -205,7 +207,7 @@ __global__ __launch_bounds__(256) void order_kernel(const int* __restrict__ ccou
     }
   }
   __syncthreads();
-  for (int u = tid; u < units; u += 256) sorted[atomicAdd(&start[min(max(cnt[u], 0), NB)], 1)] = u;
+  for (int u = tid; u < units; u += 256) sorted[atomicAdd(&start[min(max(cnt[u], 0), maxlen)], 1)] = u;
   __syncthreads();
   int* ph = perm + static_cast<size_t>(h) * 8 * per_xcd;
   for (int pos = tid; pos < 8 * per_xcd; pos += 256) {
@@ -746,7 +748,7 @@ hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const v
     const int per_xcd = (units + 7) / 8;
     int* perm = reinterpret_cast<int*>(base + w.perm_off);
     hipLaunchKernelGGL(order_kernel, dim3(p.heads), dim3(256), 0, stream, ccount, head_active, perm, p.nb,
-                       units, per_xcd);
+                       units, per_xcd, p.nb);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int grid = 8 * per_xcd * p.heads;
@@ -982,7 +984,7 @@ __global__ __launch_bounds__(256) void cl_table_kernel(const int* __restrict__ c
 }
 
 struct ClAttnWs {
-  size_t kp_off, vp_off, pstart_off, ostart_off, csize_off, tcount_off, table_off, total;
+  size_t kp_off, vp_off, pstart_off, ostart_off, csize_off, tcount_off, table_off, perm_off, total;
   int Np, stride;
 };
 
@@ -1002,7 +1004,9 @@ ClAttnWs cl_attn_ws_layout(const Problem& p) {
   w.csize_off = w.ostart_off + al(4 * rows);
   w.tcount_off = w.csize_off + al(4 * rows);
   w.table_off = w.tcount_off + al(4 * rows);
-  w.total = w.table_off + al(4 * rows * w.stride);
+  w.perm_off = w.table_off + al(4 * rows * w.stride);
+  // dispatch order (bf16 path): per head 8 eighths of ceil(NB / 8) query blocks
+  w.total = w.perm_off + (p.dtype == 0 ? al(4 * static_cast<size_t>(p.heads) * 8 * ((p.nb + 7) / 8)) : 0);
   return w;
 }
 
@@ -1041,10 +1045,16 @@ hipError_t launch_cluster_attn_t(const Problem& p, const void* q, const void* k,
     // three-wave register budget
     constexpr int kNbuf = B == 128 ? 4 : 3;
     using S = AttnShape<D, B, 32, kNbuf>;
-    const int grid = 8 * ((p.nb + 7) / 8) * p.heads;
+    const int per_xcd = (p.nb + 7) / 8;
+    int* perm = reinterpret_cast<int*>(base + w.perm_off);
+    // balanced by sub-tile count (lengths past kMaxNB share the top rank)
+    hipLaunchKernelGGL(order_kernel, dim3(p.heads), dim3(256), 0, stream, tcount, nullptr, perm, p.nb, p.nb,
+                       per_xcd, min(w.stride, kMaxNB));
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const int grid = 8 * per_xcd * p.heads;
     hipLaunchKernelGGL((attn_bf16_kernel<D, B, 32, kNbuf, true>), dim3(grid), dim3(S::kThreads), 0, stream,
                        static_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(base + w.kp_off),
-                       reinterpret_cast<const uint16_t*>(base + w.vp_off), tcount, table, nullptr, nullptr,
+                       reinterpret_cast<const uint16_t*>(base + w.vp_off), tcount, table, nullptr, perm,
                        static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2, w.Np, w.Np, w.stride);
   } else {
     hipLaunchKernelGGL((attn_f32_kernel<D, B, true>), dim3(p.heads * p.nb), dim3(B), 0, stream,

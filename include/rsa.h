@@ -399,7 +399,8 @@ rsa_status rsa_score_clusters(const rsa_problem* p, const void* q, const float* 
  * 256-byte aligned: padded k and v (bf16: v transposed), Np = tokens +
  * 31 * NB rounded up to 32 keys per head; cluster starts (padded and in
  * `order`) and the sizes as used; per-row sub-tile counts and tables of
- * Np / 32 entries.
+ * Np / 32 entries; (bf16 only) the workgroup dispatch order, heads * 8 *
+ * ceil(NB / 8) * 4 bytes.
  * Non-finite values in q, k or v give undefined results.
  */
 rsa_status rsa_cluster_attn(const rsa_problem* p, const void* q, const void* k, const void* v, const int32_t* sizes,

@@ -85,7 +85,7 @@ def test_workspace_sizes():
     npad = -(-(75600 + 31 * 591) // 32) * 32
     rows = 40 * 591
     assert B.workspace_bytes(p, B.OP_CLUSTER_ATTN) == (2 * al(2 * 40 * npad * 128) + 4 * al(4 * rows)
-                                                       + al(4 * rows * (npad // 32)))
+                                                       + al(4 * rows * (npad // 32)) + al(4 * 40 * 8 * 74))
     # query-pooled scorer: pooled q and k, then block maxima
     assert B.workspace_bytes(p, B.OP_POOLED) == 2 * al(4 * 40 * 591 * 128) + al(4 * 40 * 591)
     assert B.workspace_bytes(prob(d=96), B.OP_SCORE) == 0          # invalid problem -> 0
