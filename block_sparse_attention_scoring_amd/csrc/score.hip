@@ -207,8 +207,11 @@ __device__ __forceinline__ void lds_store_f32(float* p, float v) {
 
 // kColMask: key "blocks" are clusters, some possibly empty (colsize 0); an
 // empty cluster takes no part in any query's softmax and scores 0.
-template <typename T, int D, int B, int NBUF, bool kColMask = false>
-__global__ __launch_bounds__(2 * B, 2) void score_kernel(
+// BQ < B: the workgroup's B rows are B / BQ consecutive query blocks of BQ
+// tokens (waves of block P*B/BQ + w / (BQ/32)), each with its own weight and
+// score row, so 64-token blocks still run four waves per workgroup.
+template <typename T, int D, int B, int NBUF, bool kColMask = false, int BQ = B>
+__global__ __launch_bounds__(2 * B, NBUF == 3 ? 3 : 2) void score_kernel(
     const T* __restrict__ q, const _Float16* __restrict__ khi, const _Float16* __restrict__ klo,
     const float* __restrict__ inv_t, const uint8_t* __restrict__ head_active,
     const int* __restrict__ colsize, float* __restrict__ scores, int N, int NB, int NBp) {
@@ -228,14 +231,19 @@ __global__ __launch_bounds__(2 * B, 2) void score_kernel(
   __shared__ float part[2][kWaves][32];
   __shared__ float qconst[kWaves][2][32];  // per query of a wave: scale, -max - log2(weight)
 
+  constexpr int kBlk = B / BQ, kWpb = BQ / 32;  // query blocks per workgroup, waves per block
+  static_assert(BQ % 32 == 0 && B % BQ == 0, "whole waves per query block");
+  const int units = (NB + kBlk - 1) / kBlk;
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
-  const int h = tile / NB, I = tile - h * NB;
+  const int h = tile / units, P = tile - h * units;
   if (head_active != nullptr && head_active[h] == 0) return;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, col = lane & 31;
-  const int q0 = I * B, bI = min(B, N - q0);
-  const bool qvalid = wave * 32 + col < bI;
+  const int sub = wave / kWpb, I = P * kBlk + sub;  // this wave's query block (I >= NB: none)
+  const int q0 = I * BQ, bI = I < NB ? min(BQ, N - q0) : 0;
+  const int wrow = (wave % kWpb) * 32;  // first row of this wave inside its block
+  const bool qvalid = wrow + col < bI;
 
   // ---- this lane's query values (row wave*32+col, columns 16s+8hl..+7)
   f16x8 qh[kKS], ql[kSplitQ ? kKS : 1];
@@ -243,7 +251,7 @@ __global__ __launch_bounds__(2 * B, 2) void score_kernel(
   {
     float x[kKS][8];
     // rows past the last token read row q0 and are zeroed
-    const T* src = q + (static_cast<size_t>(h) * N + q0 + (qvalid ? wave * 32 + col : 0)) * D + 8 * hl;
+    const T* src = q + (static_cast<size_t>(h) * N + (qvalid ? q0 + wrow + col : 0)) * D + 8 * hl;
     const float keep = qvalid ? 1.f : 0.f;
     float a = 0.f;
 #pragma unroll
@@ -325,19 +333,24 @@ __global__ __launch_bounds__(2 * B, 2) void score_kernel(
 
   float mraw = -INFINITY, z = 0.f;  // pass 1, this half's key blocks
   float qs[16], qm[16];              // pass 2: per register (query) constants
-  float* srow = scores + (static_cast<size_t>(h) * NB + I) * NB;
+  // score row written by this lane in finish(): block P*kBlk + hl (lanes of
+  // wave 0, one lane half per block)
+  static_assert(kBlk <= 2, "one lane half of wave 0 per query block");
+  const int Iw = P * kBlk + hl;
+  float* srow = scores + (static_cast<size_t>(h) * NB + min(Iw, NB - 1)) * NB;
   // column 32c + col of this lane holds keys (cluster mode)
   auto live_col = [&](int c) __attribute__((always_inline)) {
     const int j = 32 * c + col;
     return j < NB && colsize[static_cast<size_t>(h) * NB + j] > 0;
   };
-  // all waves' partial sums of chunk c are in part[c & 1]
+  // all waves' partial sums of chunk c are in part[c & 1]; each block's
+  // waves are added in wave order
   auto finish = [&](int c) __attribute__((always_inline)) {
-    if (wave == 0 && lane < 32 && 32 * c + lane < NB) {
+    if (wave == 0 && hl < kBlk && Iw < NB && 32 * c + col < NB) {
       float t = 0.f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) t += part[c & 1][w][lane];
-      srow[32 * c + lane] = t;
+      for (int w = 0; w < kWpb; ++w) t += part[c & 1][hl * kWpb + w][col];
+      srow[32 * c + col] = t;
     }
   };
   auto body = [&](int u, const _Float16* cur) __attribute__((always_inline)) {
@@ -454,14 +467,17 @@ hipError_t launch_scoring_t(const Problem& p, const void* q, const void* k,
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int grid = p.heads * p.nb;
+  // bf16, 128-token blocks: a ring of three slots (48 KB), three workgroups
+  // per CU (a third wave per SIMD); fp32 queries need more registers
+  constexpr int kNbuf = std::is_same_v<T, uint16_t> ? 3 : 4;
   if (p.block == 128)
-    hipLaunchKernelGGL((score_kernel<T, D, 128, 4>), dim3(grid), dim3(256), 0, stream,
+    hipLaunchKernelGGL((score_kernel<T, D, 128, kNbuf>), dim3(grid), dim3(256), 0, stream,
                        static_cast<const T*>(q), ws.khi, ws.klo, ws.inv_t, head_active, nullptr, scores,
                        p.tokens, p.nb, NBp);
-  else
-    hipLaunchKernelGGL((score_kernel<T, D, 64, 4>), dim3(grid), dim3(128), 0, stream,
-                       static_cast<const T*>(q), ws.khi, ws.klo, ws.inv_t, head_active, nullptr, scores,
-                       p.tokens, p.nb, NBp);
+  else  // 64-token blocks: two per four-wave workgroup
+    hipLaunchKernelGGL((score_kernel<T, D, 128, kNbuf, false, 64>), dim3(p.heads * ((p.nb + 1) / 2)), dim3(256),
+                       0, stream, static_cast<const T*>(q), ws.khi, ws.klo, ws.inv_t, head_active, nullptr,
+                       scores, p.tokens, p.nb, NBp);
   return hipGetLastError();
 }
 
@@ -498,14 +514,15 @@ hipError_t launch_cluster_scoring_t(const Problem& p, const void* q, const float
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int grid = p.heads * p.nb;
+  constexpr int kNbuf = std::is_same_v<T, uint16_t> ? 3 : 4;
   if (p.block == 128)
-    hipLaunchKernelGGL((score_kernel<T, D, 128, 4, true>), dim3(grid), dim3(256), 0, stream,
+    hipLaunchKernelGGL((score_kernel<T, D, 128, kNbuf, true>), dim3(grid), dim3(256), 0, stream,
                        static_cast<const T*>(q), ws.khi, ws.klo, ws.inv_t, nullptr, sizes, scores, p.tokens,
                        p.nb, NBp);
-  else
-    hipLaunchKernelGGL((score_kernel<T, D, 64, 4, true>), dim3(grid), dim3(128), 0, stream,
-                       static_cast<const T*>(q), ws.khi, ws.klo, ws.inv_t, nullptr, sizes, scores, p.tokens,
-                       p.nb, NBp);
+  else  // 64-token blocks: two per four-wave workgroup
+    hipLaunchKernelGGL((score_kernel<T, D, 128, kNbuf, true, 64>), dim3(p.heads * ((p.nb + 1) / 2)), dim3(256),
+                       0, stream, static_cast<const T*>(q), ws.khi, ws.klo, ws.inv_t, nullptr, sizes, scores,
+                       p.tokens, p.nb, NBp);
   return hipGetLastError();
 }
 
