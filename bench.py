@@ -66,9 +66,10 @@ def source_hash(path):
     return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
 
 
-def profiled_traffic():
-    """HBM bytes per attention launch from the committed PMC summary, if current."""
-    if not os.path.exists(ATTN_PROFILE):
+def profiled_traffic(workload):
+    """HBM bytes per attention launch from the committed PMC summary, if it
+    covers this workload and the current attention source."""
+    if workload != WORKLOAD or not os.path.exists(ATTN_PROFILE):
         return None
     text = open(ATTN_PROFILE).read()
     m_hash = re.search(r"attn\.hip sha256\[:16\]: (\w+)", text)
@@ -602,7 +603,7 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": profiled_traffic(),
+            "traffic": profiled_traffic(wl.name),
             "kernel": "attn_bf16_kernel<128,128,32,3>",
             # HIP events bracket the whole library call, which also runs the
             # V^T relayout and list canonicalisation kernels (about 1%)
