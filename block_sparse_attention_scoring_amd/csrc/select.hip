@@ -20,6 +20,11 @@
 #include "common.h"
 #include "kernels.h"
 
+// The sort network asks for full unrolling at every row width; for the
+// widest rows the compiler may keep some loops (its size limit), which is
+// correct, only slower, so that remark is not reported.
+#pragma clang diagnostic ignored "-Wpass-failed"
+
 namespace rsa {
 namespace {
 
@@ -62,19 +67,34 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_kernel(
   const size_t row = static_cast<size_t>(row_id);
   const float* srow = scores + row * NB;
 
-  // key of block j (padding past NB sorts last)
-  auto key_of = [&](int j) {
-    return j < NB ? (static_cast<uint64_t>(~order_bits(srow[j])) << 32) | static_cast<uint32_t>(j) : ~0ull;
+  // key of block j with score s (block index in the low word)
+  auto key_of = [](float s, int j) {
+    return (static_cast<uint64_t>(~order_bits(s)) << 32) | static_cast<uint32_t>(j);
   };
-  // the row: lane holds indices lane*E .. lane*E + E - 1
+  // the row: lane holds indices lane*E .. lane*E + E - 1; its scores stay in
+  // registers for the mask and list at the end (padding past NB sorts last)
   uint64_t v[E];
+  float sv[E];
 #pragma unroll
-  for (int e = 0; e < E; ++e) v[e] = key_of(lane * E + e);
-  // ascending bitonic sort of the MP keys
-#pragma unroll 1
-  for (int size = 2; size <= MP; size <<= 1) {
-#pragma unroll 1
-    for (int stride = size >> 1; stride >= E; stride >>= 1) {
+  for (int e = 0; e < E; ++e) {
+    const int j = lane * E + e;
+    sv[e] = j < NB ? srow[j] : 0.f;
+  }
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    const int j = lane * E + e;
+    v[e] = j < NB ? key_of(sv[e], j) : ~0ull;
+  }
+  // ascending bitonic sort of the MP keys (counted loops, fully unrolled:
+  // every size and stride is a compile-time constant)
+  constexpr int kLogMP = __builtin_ctz(MP);
+#pragma unroll
+  for (int ls = 1; ls <= kLogMP; ++ls) {
+    const int size = 1 << ls;
+#pragma unroll
+    for (int ts = 1; ts <= ls; ++ts) {
+      const int stride = size >> ts;
+      if (stride < E) continue;
       const int dl = stride / E;
 #pragma unroll
       for (int e = 0; e < E; ++e) {
@@ -135,14 +155,14 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_kernel(
   thr = __shfl(thr, rk / E);
 
   // mask and ascending list from the unsorted row (keys rebuilt from the
-  // scores: the row is still in cache; keys are unique, so exactly k* pass)
+  // scores held in registers; keys are unique, so exactly k* pass)
   uint8_t* mrow = mask + row * NB;
   int cnt = 0;
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = lane * E + e;
     if (j < NB) {
-      const bool keep = key_of(j) <= thr;
+      const bool keep = key_of(sv[e], j) <= thr;
       mrow[j] = keep ? 1 : 0;
       cnt += keep;
     }
@@ -153,7 +173,7 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_kernel(
 #pragma unroll
   for (int e = 0; e < E; ++e) {
     const int j = lane * E + e;
-    if (j < NB && key_of(j) <= thr) irow[pos++] = j;
+    if (j < NB && key_of(sv[e], j) <= thr) irow[pos++] = j;
   }
   if (lane == 0) counts[row] = kstar;
 }
