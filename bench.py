@@ -18,7 +18,8 @@ over the timed steps with HIP events recorded on the stream the library
 launches on.  The oracle (fp64 NumPy) is timed on a bounded sample on the
 host cores as a CPU baseline, and the vendor bf16 GEMM (hipBLASLt through
 torch.matmul) is timed after the steps as the matrix-core rate this GPU
-sustains under load (roofline.vendor_gemm).
+sustains under load (roofline.vendor_gemm), and a plain device copy as the
+HBM rate it sustains (vendor_copy).
 """
 from __future__ import annotations
 
@@ -48,7 +49,7 @@ def parse():
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true", help="skip the oracle timing")
     ap.add_argument("--no-gemm-reference", action="store_true",
-                    help="skip timing the vendor bf16 GEMM next to the attention kernel")
+                    help="skip timing the vendor bf16 GEMM and device copy after the steps")
     ap.add_argument("--retrieval", action="store_true",
                     help="report block retrieval accuracy (dense mass captured at equal density) instead")
     ap.add_argument("--correction", action="store_true",
@@ -176,6 +177,29 @@ def gemm_reference(dev, n=8192, reps=40, trials=3):
         torch.cuda.synchronize()
         rates.append(2.0 * n ** 3 * reps / (e0.elapsed_time(e1) * 1e-3) / 1e12)
     del a, b, c
+    return float(sorted(rates)[len(rates) // 2])
+
+
+def copy_reference(dev, mib=1024, reps=10, trials=3):
+    """Sustained HBM rate of this GPU as a plain device copy reaches it:
+    torch's copy of `mib` MiB, read plus written bytes over the time of `reps`
+    back-to-back copies (HIP events), median of `trials` runs.  Context for
+    the bandwidth-bound kernels (drift, V relayout, pooling)."""
+    import torch
+    n = mib * (1 << 20)
+    a = torch.empty(n, dtype=torch.uint8, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    rates = []
+    for _ in range(trials):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(reps):
+            b.copy_(a)
+        e1.record()
+        torch.cuda.synchronize()
+        rates.append(2.0 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    del a, b
     return float(sorted(rates)[len(rates) // 2])
 
 
@@ -615,6 +639,11 @@ def main():
         res["roofline"]["vendor_gemm"] = {
             "value": round(gemm, 1), "unit": "TFLOP/s", "attn_frac": round(attn_tflops / gemm, 4),
             "what": "torch.matmul bf16 8192^3 (hipBLASLt), same GPU, after the timed steps",
+        }
+        copy = copy_reference(dev)
+        res["vendor_copy"] = {
+            "value": round(copy, 1), "unit": "GB/s", "drift_over_copy": round(drift_bytes / (per["drift"] * 1e-3) / 1e9 / copy, 4),
+            "what": "torch copy of 1 GiB (bytes read + written), same GPU, after the timed steps",
         }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(inp, wl, c_h, i_h, flops)
