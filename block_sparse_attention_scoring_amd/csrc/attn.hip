@@ -20,6 +20,9 @@
 // The online softmax runs in fp32 in the log2 domain, and rescales the
 // output only when the running maximum grows by more than 2^8 (exact: the
 // final normalisation uses the same reference maximum).
+#include <algorithm>
+#include <cmath>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -155,35 +158,61 @@ __global__ __launch_bounds__(256) void pair_canon_kernel(const int* __restrict__
   if (tid == 0) ccount[static_cast<size_t>(h) * NB + P] = base;
 }
 
-// Dispatch order of one head's units (query blocks, or pairs of them) over
-// the 8 XCDs.  Units are ranked by list length (ccount, clamped to
-// [0, maxlen], maxlen <= kMaxNB), longest first (counting sort; units of
-// equal length in any order), and dealt in a snake
-// over the XCDs: ranks 0-7 to XCDs 0..7, ranks 8-15 to XCDs 7..0, and so on.
-// Every XCD gets an eighth of the head's work, longest walks first, so the
-// XCDs finish together and the grid's tail holds only short walks.
-// perm[h, x, r] is the unit XCD x runs r-th for head h, or -1 where the
-// eighth is one short.  One workgroup per head; skipped for inactive heads.
+// Heads taken together by the dispatch order: ng groups of nearly equal size
+// (the first H mod ng groups hold one head more), so a group's K and V^T
+// stay in the 256 MB Infinity Cache together and hold at most kMaxOrder
+// units.
+constexpr int kMaxOrder = 4096;                       // units per group, at most
+constexpr double kGroupBytes = 160.0 * 1024 * 1024;  // K + V^T bytes per group, about
+
+struct HeadGroups {
+  int ng, per_xcd;  // groups; units per XCD per group (the largest group)
+};
+
+HeadGroups head_groups(const Problem& p, int units) {
+  const double head_bytes = 2.0 * p.tokens * p.head_dim * (p.dtype == 0 ? 2.0 : 4.0);
+  int ng = static_cast<int>(std::ceil(p.heads * head_bytes / kGroupBytes));
+  ng = std::min(std::max(ng, 1), p.heads);
+  while (ng < p.heads && (p.heads + ng - 1) / ng * units > kMaxOrder) ++ng;
+  const int gmax = (p.heads + ng - 1) / ng;
+  return {ng, (gmax * units + 7) / 8};
+}
+
+// Dispatch order over the 8 XCDs, one workgroup per head group.  The
+// group's units (query blocks, or pairs of them, of all its heads) are ranked
+// by list length (ccount, clamped to [0, maxlen], maxlen <= kMaxNB; inactive
+// heads count 0), longest first (counting sort; equal lengths in any order),
+// and dealt in a snake over the XCDs: ranks 0-7 to XCDs 0..7, ranks 8-15 to
+// XCDs 7..0, and so on.  Every XCD gets an eighth of the group's work,
+// longest walks first, so the XCDs finish together and the grid's tail holds
+// only short walks; the groups follow one another, so the XCDs share one
+// group's K/V at a time.  perm[g, x, r] = (h - first head of g) * units +
+// unit for the r-th workgroup XCD x runs in group g, or -1.
 __global__ __launch_bounds__(256) void order_kernel(const int* __restrict__ ccount,
                                                     const uint8_t* __restrict__ head_active,
-                                                    int* __restrict__ perm, int NB, int units, int per_xcd,
-                                                    int maxlen) {
+                                                    int* __restrict__ perm, int H, int NB, int units, int ng,
+                                                    int per_xcd, int maxlen) {
   constexpr int kPer = (kMaxNB + 1 + 255) / 256;  // lengths 0..maxlen
   __shared__ int start[kMaxNB + 1];  // per length: first rank, then next free rank
-  __shared__ int sorted[kMaxNB];     // unit of each rank
+  __shared__ int sorted[kMaxOrder];  // unit of each rank
   __shared__ int part[256];
-  const int h = blockIdx.x, tid = threadIdx.x;
-  if (head_active != nullptr && head_active[h] == 0) return;
-  const int* cnt = ccount + static_cast<size_t>(h) * NB;
+  const int g = blockIdx.x, tid = threadIdx.x;
+  const int base = H / ng, rem = H % ng;
+  const int h0 = g * base + min(g, rem), n = (base + (g < rem ? 1 : 0)) * units;
+  auto length = [&](int e) {
+    const int h = h0 + e / units;
+    if (head_active != nullptr && head_active[h] == 0) return 0;
+    return min(max(ccount[static_cast<size_t>(h) * NB + e % units], 0), maxlen);
+  };
   for (int i = tid; i <= maxlen; i += 256) start[i] = 0;
   __syncthreads();
-  for (int u = tid; u < units; u += 256) atomicAdd(&start[min(max(cnt[u], 0), maxlen)], 1);
+  for (int e = tid; e < n; e += 256) atomicAdd(&start[length(e)], 1);
   __syncthreads();
   // exclusive scan over lengths maxlen, ..., 0 (longest first): thread t
   // takes positions [t*kPer, (t+1)*kPer) of that descending order
   int local = 0;
-  for (int e = 0; e < kPer; ++e) {
-    const int len = maxlen - (tid * kPer + e);
+  for (int k = 0; k < kPer; ++k) {
+    const int len = maxlen - (tid * kPer + k);
     if (len >= 0) local += start[len];
   }
   part[tid] = local;
@@ -198,8 +227,8 @@ __global__ __launch_bounds__(256) void order_kernel(const int* __restrict__ ccou
   }
   __syncthreads();
   int run = part[tid];
-  for (int e = 0; e < kPer; ++e) {
-    const int len = maxlen - (tid * kPer + e);
+  for (int k = 0; k < kPer; ++k) {
+    const int len = maxlen - (tid * kPer + k);
     if (len >= 0) {
       const int c = start[len];
       start[len] = run;
@@ -207,13 +236,13 @@ __global__ __launch_bounds__(256) void order_kernel(const int* __restrict__ ccou
     }
   }
   __syncthreads();
-  for (int u = tid; u < units; u += 256) sorted[atomicAdd(&start[min(max(cnt[u], 0), maxlen)], 1)] = u;
+  for (int e = tid; e < n; e += 256) sorted[atomicAdd(&start[length(e)], 1)] = e;
   __syncthreads();
-  int* ph = perm + static_cast<size_t>(h) * 8 * per_xcd;
+  int* pg = perm + static_cast<size_t>(g) * 8 * per_xcd;
   for (int pos = tid; pos < 8 * per_xcd; pos += 256) {
     const int x = pos / per_xcd, row = pos % per_xcd;
     const int r = row * 8 + ((row & 1) ? 7 - x : x);
-    ph[pos] = r < units ? sorted[r] : -1;
+    pg[pos] = r < n ? sorted[r] : -1;
   }
 }
 
@@ -298,7 +327,7 @@ __global__ __launch_bounds__(2 * B, NBUF == 3 ? 3 : 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ vt, const int* __restrict__ ccount,
     const int* __restrict__ clist, const uint8_t* __restrict__ head_active, const int* __restrict__ perm,
     uint16_t* __restrict__ out, float* __restrict__ lse, int H, int N, int NB, float scale_log2,
-    int Nk, int Nv, int lstride) {
+    int Nk, int Nv, int lstride, int ng, int per_xcd) {
   using S = AttnShape<D, B, KS, NBUF>;
   static_assert(NBUF >= 3 && NBUF <= 4, "ring of 3 or 4 LDS slots");
   static_assert(!kTable || KS == 32, "table entries are 32-key sub-tiles");
@@ -314,20 +343,19 @@ __global__ __launch_bounds__(2 * B, NBUF == 3 ? 3 : 2) void attn_bf16_kernel(
   __shared__ __attribute__((aligned(1024))) uint16_t slot2[NBUF > 2 ? 2 * S::kTile : 8];
   __shared__ __attribute__((aligned(1024))) uint16_t slot3[NBUF > 3 ? 2 * S::kTile : 8];
 
-  // Head-synchronous schedule: workgroup ids go round-robin over the 8 XCDs;
-  // XCD x takes an eighth of the units of one head after another, so all
-  // XCDs share one head's K/V at a time.  With perm (order_kernel) the
-  // eighths are balanced by list length, longest walks first; without it
-  // XCD x takes the x-th contiguous eighth in order.
+  // Group-synchronous schedule: workgroup ids go round-robin over the 8
+  // XCDs; XCD x takes the x-th eighth of one head group's units after
+  // another (order_kernel: balanced by list length, longest walks first), so
+  // all XCDs share one group's K/V at a time.
   const int units = kPair ? (NB + 1) / 2 : NB;  // query blocks, or pairs of them
-  const int per_xcd = (units + 7) / 8;
   const int xcd = blockIdx.x & 7, slot = blockIdx.x >> 3;
-  const int h = slot / per_xcd;
-  if (h >= H) return;
+  const int g = slot / per_xcd;
+  if (g >= ng) return;
+  const int e = perm[static_cast<size_t>(g) * 8 * per_xcd + xcd * per_xcd + slot % per_xcd];
+  if (e < 0) return;
+  const int h = g * (H / ng) + min(g, H % ng) + e / units, I = e % units;
+  if (h >= H || I >= units) return;
   if (head_active != nullptr && head_active[h] == 0) return;
-  const int pos = xcd * per_xcd + slot % per_xcd;
-  const int I = perm != nullptr ? perm[static_cast<size_t>(h) * 8 * per_xcd + pos] : pos;
-  if (I < 0 || I >= units) return;
 
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform: LDS addresses stay scalar
@@ -708,8 +736,9 @@ AttnWs attn_ws_layout(const Problem& p) {
   w.ccount_off = p.dtype == 0 ? al(sizeof(uint16_t) * p.heads * p.head_dim * static_cast<size_t>(p.nb) * p.block) : 0;
   w.clist_off = w.ccount_off + al(sizeof(int) * rows);
   w.perm_off = w.clist_off + al(sizeof(int) * rows * p.nb);
-  // dispatch order (bf16 path): per head 8 eighths of ceil(NB / 8) units
-  w.total = w.perm_off + (p.dtype == 0 ? al(sizeof(int) * p.heads * 8 * static_cast<size_t>((p.nb + 7) / 8)) : 0);
+  // dispatch order (bf16 path): per head group 8 eighths of its units
+  const HeadGroups hg = head_groups(p, p.block == 64 ? (p.nb + 1) / 2 : p.nb);
+  w.total = w.perm_off + (p.dtype == 0 ? al(sizeof(int) * 8 * static_cast<size_t>(hg.ng) * hg.per_xcd) : 0);
   return w;
 }
 
@@ -745,17 +774,17 @@ hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const v
     e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int units = kPairs ? (p.nb + 1) / 2 : p.nb;
-    const int per_xcd = (units + 7) / 8;
+    const HeadGroups hg = head_groups(p, units);
     int* perm = reinterpret_cast<int*>(base + w.perm_off);
-    hipLaunchKernelGGL(order_kernel, dim3(p.heads), dim3(256), 0, stream, ccount, head_active, perm, p.nb,
-                       units, per_xcd, p.nb);
+    hipLaunchKernelGGL(order_kernel, dim3(hg.ng), dim3(256), 0, stream, ccount, head_active, perm, p.heads, p.nb,
+                       units, hg.ng, hg.per_xcd, p.nb);
     e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int grid = 8 * per_xcd * p.heads;
+    const int grid = 8 * hg.per_xcd * hg.ng;
     hipLaunchKernelGGL((attn_bf16_kernel<D, kRows, kKs, kNbuf, false, B>), dim3(grid), dim3(S::kThreads), 0,
                        stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt, ccount,
                        clist, head_active, perm, static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2,
-                       p.tokens, p.nb * B, p.nb);
+                       p.tokens, p.nb * B, p.nb, hg.ng, hg.per_xcd);
   } else {
     hipLaunchKernelGGL((attn_f32_kernel<D, B>), dim3(p.heads * p.nb), dim3(B), 0, stream,
                        static_cast<const float*>(q), static_cast<const float*>(k),
@@ -1005,8 +1034,9 @@ ClAttnWs cl_attn_ws_layout(const Problem& p) {
   w.tcount_off = w.csize_off + al(4 * rows);
   w.table_off = w.tcount_off + al(4 * rows);
   w.perm_off = w.table_off + al(4 * rows * w.stride);
-  // dispatch order (bf16 path): per head 8 eighths of ceil(NB / 8) query blocks
-  w.total = w.perm_off + (p.dtype == 0 ? al(4 * static_cast<size_t>(p.heads) * 8 * ((p.nb + 7) / 8)) : 0);
+  // dispatch order (bf16 path): per head group 8 eighths of its query blocks
+  const HeadGroups hg = head_groups(p, p.nb);
+  w.total = w.perm_off + (p.dtype == 0 ? al(4 * 8 * static_cast<size_t>(hg.ng) * hg.per_xcd) : 0);
   return w;
 }
 
@@ -1045,17 +1075,18 @@ hipError_t launch_cluster_attn_t(const Problem& p, const void* q, const void* k,
     // three-wave register budget
     constexpr int kNbuf = B == 128 ? 4 : 3;
     using S = AttnShape<D, B, 32, kNbuf>;
-    const int per_xcd = (p.nb + 7) / 8;
+    const HeadGroups hg = head_groups(p, p.nb);
     int* perm = reinterpret_cast<int*>(base + w.perm_off);
     // balanced by sub-tile count (lengths past kMaxNB share the top rank)
-    hipLaunchKernelGGL(order_kernel, dim3(p.heads), dim3(256), 0, stream, tcount, nullptr, perm, p.nb, p.nb,
-                       per_xcd, min(w.stride, kMaxNB));
+    hipLaunchKernelGGL(order_kernel, dim3(hg.ng), dim3(256), 0, stream, tcount, nullptr, perm, p.heads, p.nb,
+                       p.nb, hg.ng, hg.per_xcd, std::min(w.stride, kMaxNB));
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const int grid = 8 * per_xcd * p.heads;
+    const int grid = 8 * hg.per_xcd * hg.ng;
     hipLaunchKernelGGL((attn_bf16_kernel<D, B, 32, kNbuf, true>), dim3(grid), dim3(S::kThreads), 0, stream,
                        static_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(base + w.kp_off),
                        reinterpret_cast<const uint16_t*>(base + w.vp_off), tcount, table, nullptr, perm,
-                       static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2, w.Np, w.Np, w.stride);
+                       static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2, w.Np, w.Np, w.stride, hg.ng,
+                       hg.per_xcd);
   } else {
     hipLaunchKernelGGL((attn_f32_kernel<D, B, true>), dim3(p.heads * p.nb), dim3(B), 0, stream,
                        static_cast<const float*>(q), reinterpret_cast<const float*>(base + w.kp_off),

@@ -228,7 +228,8 @@ rsa_status rsa_mask_drift(const rsa_problem* p, const void* q, const void* k,
  *   invalid entries; bf16 with block 64: the union of query blocks 2P and
  *   2P+1 per pair, with membership bits): counts, heads * NB * 4 bytes, and
  *   lists, heads * NB * NB * 4 bytes; then (bf16 only) the workgroup
- *   dispatch order, heads * 8 * ceil(NB / 8) * 4 bytes.
+ *   dispatch order, 4 bytes per query block (per pair of 64-token blocks)
+ *   plus padding to whole eighths of each head group.
  * Non-finite values in q, k or v give undefined results.
  */
 rsa_status rsa_block_sparse_attn(const rsa_problem* p, const void* q, const void* k,
@@ -399,8 +400,8 @@ rsa_status rsa_score_clusters(const rsa_problem* p, const void* q, const float* 
  * 256-byte aligned: padded k and v (bf16: v transposed), Np = tokens +
  * 31 * NB rounded up to 32 keys per head; cluster starts (padded and in
  * `order`) and the sizes as used; per-row sub-tile counts and tables of
- * Np / 32 entries; (bf16 only) the workgroup dispatch order, heads * 8 *
- * ceil(NB / 8) * 4 bytes.
+ * Np / 32 entries; (bf16 only) the workgroup dispatch order, 4 bytes per
+ * query block plus padding to whole eighths of each head group.
  * Non-finite values in q, k or v give undefined results.
  */
 rsa_status rsa_cluster_attn(const rsa_problem* p, const void* q, const void* k, const void* v, const int32_t* sizes,

@@ -68,7 +68,8 @@ def test_workspace_sizes():
     # attention: v re-laid out key-major (bf16), then the canonical list
     # counts and lists of every row, then (bf16) the dispatch order
     lists = al(4 * 40 * 591) + al(4 * 40 * 591 * 591)
-    order = al(4 * 40 * 8 * 74)
+    # 40 heads of 38.7 MB (K + V^T) in 10 groups of 4: 8 eighths of ceil(4 * 591 / 8) units
+    order = al(4 * 8 * 10 * 296)
     assert B.workspace_bytes(p, B.OP_ATTN) == al(2 * 40 * 128 * 591 * 128) + lists + order
     assert B.workspace_bytes(prob(heads=40, grid=(21, 45, 80), b=128, dtype=1), B.OP_ATTN) == lists
     # Gram matrix: one D x D fp32 partial per 2048 tokens (bf16 only)
@@ -85,7 +86,7 @@ def test_workspace_sizes():
     npad = -(-(75600 + 31 * 591) // 32) * 32
     rows = 40 * 591
     assert B.workspace_bytes(p, B.OP_CLUSTER_ATTN) == (2 * al(2 * 40 * npad * 128) + 4 * al(4 * rows)
-                                                       + al(4 * rows * (npad // 32)) + al(4 * 40 * 8 * 74))
+                                                       + al(4 * rows * (npad // 32)) + al(4 * 8 * 10 * 296))
     # query-pooled scorer: pooled q and k, then block maxima
     assert B.workspace_bytes(p, B.OP_POOLED) == 2 * al(4 * 40 * 591 * 128) + al(4 * 40 * 591)
     assert B.workspace_bytes(prob(d=96), B.OP_SCORE) == 0          # invalid problem -> 0
