@@ -306,8 +306,10 @@ def correction(args):
     plain sparse output on the same cached lists are compared with dense
     attention (the attention call given every block), as relative L2 errors.
     Then, on the last step's inputs, the omitted-block pass over every head,
-    the sparse pass and the merge are timed with HIP events on the library's
-    stream; the merge, a streaming kernel, is priced against HBM bandwidth.
+    the sparse pass, the merge and the corrected pass (sparse attention joined
+    with the cached part inside the kernel, what the cache runs) are timed
+    with HIP events on the library's stream; the merge, a streaming kernel, is
+    priced against HBM bandwidth.
     """
     import numpy as np
     import torch
@@ -370,6 +372,9 @@ def correction(args):
                                                  lse=s_lse, workspace=ws))
     m_out, m_lse = s_out.clone(), s_lse.clone()
     t_merge = timed(lambda: R.attn_merge(m_out, m_lse, o_out, o_lse, p), reps=20)
+    c_out, c_lse = torch.empty_like(q), torch.empty_like(o_lse)
+    t_corr = timed(lambda: R.block_sparse_attn_corrected(q, k, v, cache.counts, cache.block_idx, o_out, o_lse, p,
+                                                         out=c_out, lse=c_lse, workspace=ws))
     rows = wl.heads * wl.tokens
     merge_bytes = rows * (3 * wl.head_dim * 2 + 3 * 4)
     dens = float(cache.density.mean().item())
@@ -383,7 +388,7 @@ def correction(args):
         "refreshes_per_head": {"min": int(refresh_total.min()), "max": int(refresh_total.max()),
                                "mean": round(float(refresh_total.mean()), 2)},
         "ms": {"omitted_all_heads": round(t_omit, 3), "sparse": round(t_sparse, 3),
-               "merge": round(t_merge, 4)},
+               "merge": round(t_merge, 4), "corrected": round(t_corr, 3)},
         "final_density": round(dens, 4),
         "merge_roofline": {"bound": "hbm", "bytes": merge_bytes,
                            "achieved": round(merge_bytes / (t_merge * 1e-3) / 1e9, 1),

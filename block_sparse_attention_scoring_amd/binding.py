@@ -75,6 +75,7 @@ def _declare(lib):
         "rsa_score_blocks_pooled": (i32, [pp, _P, _P, _P, _P, sz, _P]),
         "rsa_attn_omitted": (i32, [pp, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
         "rsa_attn_merge": (i32, [pp, _P, _P, _P, _P, _P]),
+        "rsa_block_sparse_attn_corrected": (i32, [pp, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
         "rsa_query_gram": (i32, [pp, _P, _P, _P, sz, _P]),
         "rsa_kmeans": (i32, [pp, _P, _P, i32, i32, _P, _P, _P, _P, _P, sz, _P]),
         "rsa_score_clusters": (i32, [pp, _P, _P, _P, _P, _P, sz, _P]),
@@ -245,6 +246,23 @@ def attn_merge(out, lse, part_out, part_lse, p: Problem):
     """In place: (out, lse) <- attention over the union of two disjoint key sets."""
     _check(lib().rsa_attn_merge(ctypes.byref(p), _ptr(out), _ptr(lse), _ptr(part_out), _ptr(part_lse),
                                 _stream(out)), "rsa_attn_merge")
+    return out, lse
+
+
+def block_sparse_attn_corrected(q, k, v, counts, block_idx, part_out, part_lse, p: Problem, out=None, lse=None,
+                                workspace=None):
+    """Sparse attention over the lists joined with a cached complementary part
+    in one pass -> (out like q, lse fp32 [H, N]) (rsa_block_sparse_attn_corrected).
+    ``out``/``lse`` may be ``part_out``/``part_lse`` (in place)."""
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None:
+        lse = torch.empty((p.heads, p.tokens), dtype=torch.float32, device=q.device)
+    ws, wsb = _workspace(p, OP_ATTN, q.device, workspace)
+    _check(lib().rsa_block_sparse_attn_corrected(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(counts),
+                                                 _ptr(block_idx), _ptr(part_out), _ptr(part_lse), _ptr(out),
+                                                 _ptr(lse), _ptr(ws), wsb, _stream(q)),
+           "rsa_block_sparse_attn_corrected")
     return out, lse
 
 

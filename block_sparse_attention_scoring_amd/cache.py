@@ -82,11 +82,9 @@ class MaskCache:
                        head_active=None if self._corr_all else active, out=self.corr_out,
                        lse=self.corr_lse, workspace=self.attn_ws)
         self._corr_all = False
-        if lse is None:
-            lse = torch.empty((self.p.heads, self.p.tokens), dtype=torch.float32, device=q.device)
-        out, lse = B.block_sparse_attn(q, k, v, self.counts, self.block_idx, self.p, out=out, lse=lse,
-                                       workspace=self.attn_ws)
-        return B.attn_merge(out, lse, self.corr_out, self.corr_lse, self.p)
+        # the sparse pass joined with the cached part inside the attention kernel
+        return B.block_sparse_attn_corrected(q, k, v, self.counts, self.block_idx, self.corr_out, self.corr_lse,
+                                             self.p, out=out, lse=lse, workspace=self.attn_ws)
 
     def turbo(self, top_p: torch.Tensor, max_blocks: int | None = None):
         """RAPID Turbo mode: re-select every head on the cached scores (no re-scoring)."""

@@ -148,8 +148,8 @@ rsa_status rsa_block_sparse_attn(const rsa_problem* p, const void* q, const void
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return RSA_ERR_ALIGN;
   st = check_ws(pr, RSA_OP_ATTN, ws, ws_bytes);
   if (st != RSA_OK) return st;
-  return hip_status(rsa::launch_attention(pr, q, k, v, counts, block_idx, nullptr, 0, out, lse, ws,
-                                          stream));
+  return hip_status(rsa::launch_attention(pr, q, k, v, counts, block_idx, nullptr, 0, nullptr, nullptr, out, lse,
+                                          ws, stream));
 }
 
 rsa_status rsa_dense_block_mass(const rsa_problem* p, const void* q, const void* k, float* mass,
@@ -187,8 +187,26 @@ rsa_status rsa_attn_omitted(const rsa_problem* p, const void* q, const void* k, 
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(out)) return RSA_ERR_ALIGN;
   st = check_ws(pr, RSA_OP_ATTN, ws, ws_bytes);
   if (st != RSA_OK) return st;
-  return hip_status(rsa::launch_attention(pr, q, k, v, counts, block_idx, head_active, 1, out, lse,
-                                          ws, stream));
+  return hip_status(rsa::launch_attention(pr, q, k, v, counts, block_idx, head_active, 1, nullptr, nullptr, out,
+                                          lse, ws, stream));
+}
+
+rsa_status rsa_block_sparse_attn_corrected(const rsa_problem* p, const void* q, const void* k, const void* v,
+                                           const int32_t* counts, const int32_t* block_idx, const void* part_out,
+                                           const float* part_lse, void* out, float* lse, void* ws,
+                                           size_t ws_bytes, hipStream_t stream) {
+  rsa::Problem pr;
+  rsa_status st = make_problem(p, &pr);
+  if (st != RSA_OK) return st;
+  if (q == nullptr || k == nullptr || v == nullptr || counts == nullptr || block_idx == nullptr ||
+      part_out == nullptr || part_lse == nullptr || out == nullptr || lse == nullptr)
+    return RSA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(part_out) || !aligned16(out))
+    return RSA_ERR_ALIGN;
+  st = check_ws(pr, RSA_OP_ATTN, ws, ws_bytes);
+  if (st != RSA_OK) return st;
+  return hip_status(rsa::launch_attention(pr, q, k, v, counts, block_idx, nullptr, 0, part_out, part_lse, out,
+                                          lse, ws, stream));
 }
 
 rsa_status rsa_attn_merge(const rsa_problem* p, void* out, float* lse, const void* part_out,

@@ -326,8 +326,8 @@ __global__ __launch_bounds__(2 * B, NBUF == 3 ? 3 : 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const int* __restrict__ ccount,
     const int* __restrict__ clist, const uint8_t* __restrict__ head_active, const int* __restrict__ perm,
-    uint16_t* __restrict__ out, float* __restrict__ lse, int H, int N, int NB, float scale_log2,
-    int Nk, int Nv, int lstride, int ng, int per_xcd) {
+    const uint16_t* part, const float* part_lse, uint16_t* out, float* lse, int H, int N, int NB,
+    float scale_log2, int Nk, int Nv, int lstride, int ng, int per_xcd) {
   using S = AttnShape<D, B, KS, NBUF>;
   static_assert(NBUF >= 3 && NBUF <= 4, "ring of 3 or 4 LDS slots");
   static_assert(!kTable || KS == 32, "table entries are 32-key sub-tiles");
@@ -627,21 +627,48 @@ __global__ __launch_bounds__(2 * B, NBUF == 3 ? 3 : 2) void attn_bf16_kernel(
 
   const float l_run = (l_part[0] + l_part[1]) + (l_part[2] + l_part[3]);
   const float l_tot = l_run + __shfl_xor(l_run, 32);
-  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (qrow < N) {
-    uint16_t* dst = out + head_off + static_cast<size_t>(qrow) * D;
+    const size_t row = static_cast<size_t>(h) * N + qrow;
+    float ls = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;  // natural log
+    // out = wa * O_unnormalised + wb * cached part
+    float wa = l_tot > 0.f ? 1.f / l_tot : 0.f, wb = 0.f;
+    if (part != nullptr) {
+      // join with a cached attention over the complementary keys: the
+      // softmax over the union weighs each part by its exp(lse)
+      const float lb = part_lse[row];
+      const float m = fmaxf(ls, lb);
+      if (m > -INFINITY) {
+        const float ea = expf(ls - m), eb = expf(lb - m);  // the larger of the two is 1
+        const float z = ea + eb;
+        wa *= ea / z;
+        wb = eb / z;
+        ls = m + logf(z);
+      } else {
+        wa = 0.f;
+      }
+    }
+    uint16_t* dst = out + row * D;
+    const uint16_t* src = part != nullptr ? part + row * D : nullptr;
 #pragma unroll
     for (int dt = 0; dt < S::kDT; ++dt) {
 #pragma unroll
       for (int g = 0; g < 4; ++g) {
+        const int c = 32 * dt + 8 * g + 4 * hl;
+        float x[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e) x[e] = oacc[dt][4 * g + e] * wa;
+        if (src != nullptr) {
+          const bf16x4 b = *reinterpret_cast<const bf16x4*>(src + c);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) x[e] = fmaf(wb, static_cast<float>(b[e]), x[e]);
+        }
         bf16x4 o;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) o[e] = static_cast<__bf16>(oacc[dt][4 * g + e] * inv);
-        *reinterpret_cast<bf16x4*>(dst + 32 * dt + 8 * g + 4 * hl) = o;
+        for (int e = 0; e < 4; ++e) o[e] = static_cast<__bf16>(x[e]);
+        *reinterpret_cast<bf16x4*>(dst + c) = o;
       }
     }
-    if (lse != nullptr && hl == 0)
-      lse[static_cast<size_t>(h) * N + qrow] = l_tot > 0.f ? (m_run + __log2f(l_tot)) * kLn2 : -INFINITY;
+    if (lse != nullptr && hl == 0) lse[row] = ls;
   }
 }
 
@@ -654,7 +681,7 @@ template <int D, int B, bool kTable = false>
 __global__ __launch_bounds__(B) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int* __restrict__ ccount, const int* __restrict__ clist,
-    const uint8_t* __restrict__ head_active, float* __restrict__ out, float* __restrict__ lse,
+    const uint8_t* __restrict__ head_active, const float* part, const float* part_lse, float* out, float* lse,
     int N, int NB, float scale_log2, int Nk, int lstride) {
   constexpr int kChunk = 32;
   __shared__ float Ks[kChunk * D];
@@ -716,10 +743,28 @@ __global__ __launch_bounds__(B) void attn_f32_kernel(
     }
   }
   if (qrow < N) {
-    const float inv = l > 0.f ? 1.f / l : 0.f;
+    const size_t row = static_cast<size_t>(h) * N + qrow;
+    float ls = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+    float wa = l > 0.f ? 1.f / l : 0.f, wb = 0.f;
+    if (part != nullptr) {  // join with the cached complementary part (as attn_bf16_kernel)
+      const float lb = part_lse[row];
+      const float mm = fmaxf(ls, lb);
+      if (mm > -INFINITY) {
+        const float ea = expf(ls - mm), eb = expf(lb - mm);
+        const float z = ea + eb;
+        wa *= ea / z;
+        wb = eb / z;
+        ls = mm + logf(z);
+      } else {
+        wa = 0.f;
+      }
+    }
 #pragma unroll
-    for (int d = 0; d < D; ++d) out[head_off + static_cast<size_t>(qrow) * D + d] = o[d] * inv;
-    if (lse != nullptr) lse[static_cast<size_t>(h) * N + qrow] = l > 0.f ? (m + log2f(l)) * kLn2 : -INFINITY;
+    for (int d = 0; d < D; ++d) {
+      const float c = part != nullptr ? wb * part[row * D + d] : 0.f;
+      out[row * D + d] = fmaf(o[d], wa, c);
+    }
+    if (lse != nullptr) lse[row] = ls;
   }
 }
 
@@ -745,7 +790,8 @@ AttnWs attn_ws_layout(const Problem& p) {
 template <int D, int B>
 hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const void* v,
                          const int* counts, const int* idx, const uint8_t* head_active,
-                         int complement, void* out, float* lse, void* ws, hipStream_t stream) {
+                         int complement, const void* part, const float* part_lse, void* out, float* lse,
+                         void* ws, hipStream_t stream) {
   const float sl2 = p.scale * kLog2e;
   const AttnWs w = attn_ws_layout(p);
   char* base = static_cast<char*>(ws);
@@ -783,13 +829,15 @@ hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const v
     const int grid = 8 * hg.per_xcd * hg.ng;
     hipLaunchKernelGGL((attn_bf16_kernel<D, kRows, kKs, kNbuf, false, B>), dim3(grid), dim3(S::kThreads), 0,
                        stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt, ccount,
-                       clist, head_active, perm, static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2,
-                       p.tokens, p.nb * B, p.nb, hg.ng, hg.per_xcd);
+                       clist, head_active, perm, static_cast<const uint16_t*>(part), part_lse,
+                       static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2, p.tokens, p.nb * B, p.nb,
+                       hg.ng, hg.per_xcd);
   } else {
     hipLaunchKernelGGL((attn_f32_kernel<D, B>), dim3(p.heads * p.nb), dim3(B), 0, stream,
                        static_cast<const float*>(q), static_cast<const float*>(k),
                        static_cast<const float*>(v), ccount, clist, head_active,
-                       static_cast<float*>(out), lse, p.tokens, p.nb, sl2, p.tokens, p.nb);
+                       static_cast<const float*>(part), part_lse, static_cast<float*>(out), lse, p.tokens, p.nb,
+                       sl2, p.tokens, p.nb);
   }
   return hipGetLastError();
 }
@@ -1084,13 +1132,13 @@ hipError_t launch_cluster_attn_t(const Problem& p, const void* q, const void* k,
     const int grid = 8 * hg.per_xcd * hg.ng;
     hipLaunchKernelGGL((attn_bf16_kernel<D, B, 32, kNbuf, true>), dim3(grid), dim3(S::kThreads), 0, stream,
                        static_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(base + w.kp_off),
-                       reinterpret_cast<const uint16_t*>(base + w.vp_off), tcount, table, nullptr, perm,
-                       static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2, w.Np, w.Np, w.stride, hg.ng,
-                       hg.per_xcd);
+                       reinterpret_cast<const uint16_t*>(base + w.vp_off), tcount, table, nullptr, perm, nullptr,
+                       nullptr, static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2, w.Np, w.Np, w.stride,
+                       hg.ng, hg.per_xcd);
   } else {
     hipLaunchKernelGGL((attn_f32_kernel<D, B, true>), dim3(p.heads * p.nb), dim3(B), 0, stream,
                        static_cast<const float*>(q), reinterpret_cast<const float*>(base + w.kp_off),
-                       reinterpret_cast<const float*>(base + w.vp_off), tcount, table, nullptr,
+                       reinterpret_cast<const float*>(base + w.vp_off), tcount, table, nullptr, nullptr, nullptr,
                        static_cast<float*>(out), lse, p.tokens, p.nb, sl2, w.Np, w.stride);
   }
   return hipGetLastError();
@@ -1101,8 +1149,11 @@ size_t attn_ws_bytes(const Problem& p) { return attn_ws_layout(p).total; }
 
 hipError_t launch_attention(const Problem& p, const void* q, const void* k, const void* v,
                             const int* counts, const int* idx, const uint8_t* head_active,
-                            int complement, void* out, float* lse, void* ws, hipStream_t stream) {
-  auto go = [&](auto fn) { return fn(p, q, k, v, counts, idx, head_active, complement, out, lse, ws, stream); };
+                            int complement, const void* part, const float* part_lse, void* out, float* lse,
+                            void* ws, hipStream_t stream) {
+  auto go = [&](auto fn) {
+    return fn(p, q, k, v, counts, idx, head_active, complement, part, part_lse, out, lse, ws, stream);
+  };
   if (p.head_dim == 128 && p.block == 128) return go(launch_attn_t<128, 128>);
   if (p.head_dim == 128 && p.block == 64) return go(launch_attn_t<128, 64>);
   if (p.head_dim == 64 && p.block == 128) return go(launch_attn_t<64, 128>);

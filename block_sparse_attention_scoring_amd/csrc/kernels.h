@@ -50,9 +50,13 @@ hipError_t launch_drift(const Problem& p, const void* q, const void* k, void* q_
 // the blocks each row does not list; heads with head_active[h] == 0 (when
 // head_active is not NULL) are skipped and their outputs left untouched.
 size_t attn_ws_bytes(const Problem& p);
+// With part != NULL the result is joined with a cached attention over the
+// complementary keys (part, part_lse: [heads, tokens, head_dim] and
+// [heads, tokens]) in the epilogue; out may be part.
 hipError_t launch_attention(const Problem& p, const void* q, const void* k, const void* v,
                             const int* counts, const int* idx, const uint8_t* head_active,
-                            int complement, void* out, float* lse, void* ws, hipStream_t stream);
+                            int complement, const void* part, const float* part_lse, void* out, float* lse,
+                            void* ws, hipStream_t stream);
 // Attention with clusters as key blocks (lists name clusters): K and V are
 // gathered into a padded cluster layout, each row's clusters become a table
 // of 32-key sub-tiles, and the attention kernels walk the tables.

@@ -29,11 +29,12 @@
  * attention mass per key block, and rsa_score_blocks_pooled the comparison
  * scorer that averages the queries before the softmax.
  *
- * Two calls carry the cached correction of RECAP (Reciprocal Sparse Attention
- * and Hierarchical Caching for Efficient Video Diffusion, Abstract):
+ * Three calls carry the cached correction of RECAP (Reciprocal Sparse
+ * Attention and Hierarchical Caching for Efficient Video Diffusion, Abstract):
  * rsa_attn_omitted computes, at a mask refresh, the attention over the key
  * blocks each list leaves out, to be cached; rsa_attn_merge joins a fresh
- * sparse output with that cached part, weighted by their log-sum-exps.
+ * sparse output with that cached part, weighted by their log-sum-exps; and
+ * rsa_block_sparse_attn_corrected does both of the last in one pass.
  *
  * Common conventions
  * ------------------
@@ -315,6 +316,30 @@ rsa_status rsa_attn_omitted(const rsa_problem* p, const void* q, const void* k, 
  */
 rsa_status rsa_attn_merge(const rsa_problem* p, void* out, float* lse, const void* part_out,
                           const float* part_lse, hipStream_t stream);
+
+/*
+ * Corrected block-sparse attention: rsa_block_sparse_attn over the current
+ * lists joined, inside the same kernel, with a cached attention over the
+ * complementary keys (RECAP, Abstract, as rsa_attn_merge):
+ *
+ *   out[r,:] = exp(lse_s[r] - L) O_s[r,:] + exp(part_lse[r] - L) part_out[r,:],
+ *   lse[r]   = L = log(exp(lse_s[r]) + exp(part_lse[r])),
+ *
+ * O_s, lse_s the sparse attention of row r.  Equal to rsa_block_sparse_attn
+ * followed by rsa_attn_merge, except that O_s enters in fp32 rather than
+ * rounded to the output type first, and no separate pass reads and writes
+ * the outputs again.  Arguments as in rsa_block_sparse_attn and
+ * rsa_attn_merge; part_out ([heads, tokens, head_dim] of `dtype`, 16-byte
+ * aligned) and part_lse ([heads, tokens] fp32) are read only; lse is
+ * required.  out may be part_out and lse may be part_lse (in place: every
+ * element is read before the same thread writes it).  ws / ws_bytes: as for
+ * rsa_block_sparse_attn (RSA_OP_ATTN).
+ * Non-finite values in q, k or v give undefined results.
+ */
+rsa_status rsa_block_sparse_attn_corrected(const rsa_problem* p, const void* q, const void* k, const void* v,
+                                           const int32_t* counts, const int32_t* block_idx, const void* part_out,
+                                           const float* part_lse, void* out, float* lse, void* ws,
+                                           size_t ws_bytes, hipStream_t stream);
 
 /*
  * Gram matrix of the current queries (PARK, Abstract: the keys are transformed

@@ -43,7 +43,7 @@ def test_exports_every_declared_symbol(lib):
     assert set(names) == {"rsa_workspace_bytes", "rsa_status_str", "rsa_version", "rsa_score_blocks",
                           "rsa_select_topp", "rsa_mask_drift", "rsa_block_sparse_attn",
                           "rsa_dense_block_mass", "rsa_score_blocks_pooled", "rsa_attn_omitted",
-                          "rsa_attn_merge", "rsa_query_gram", "rsa_kmeans",
+                          "rsa_attn_merge", "rsa_block_sparse_attn_corrected", "rsa_query_gram", "rsa_kmeans",
                           "rsa_score_clusters", "rsa_cluster_attn"}
     for n in names:
         assert hasattr(lib, n), n
@@ -136,6 +136,11 @@ def test_null_problem_and_pointers(lib):
                                 b.ptr, 1 << 30, None) == NULL
     assert lib.rsa_attn_merge(ctypes.byref(p), b.ptr, b.ptr, b.ptr, None, None) == NULL
     assert lib.rsa_attn_merge(None, b.ptr, b.ptr, b.ptr, b.ptr, None) == NULL
+    # the corrected attention needs the cached part and writes an lse
+    assert lib.rsa_block_sparse_attn_corrected(ctypes.byref(p), b.ptr, b.ptr, b.ptr, b.ptr, b.ptr, None, b.ptr,
+                                               b.ptr, b.ptr, b.ptr, 1 << 30, None) == NULL
+    assert lib.rsa_block_sparse_attn_corrected(ctypes.byref(p), b.ptr, b.ptr, b.ptr, b.ptr, b.ptr, b.ptr, b.ptr,
+                                               b.ptr, None, b.ptr, 1 << 30, None) == NULL
     assert lib.rsa_query_gram(ctypes.byref(p), None, b.ptr, b.ptr, 1 << 30, None) == NULL
     assert lib.rsa_score_clusters(ctypes.byref(p), b.ptr, b.ptr, None, b.ptr, b.ptr, 1 << 30, None) == NULL
     assert lib.rsa_cluster_attn(ctypes.byref(p), b.ptr, b.ptr, b.ptr, b.ptr, None, b.ptr, b.ptr, b.ptr, b.ptr,
@@ -157,6 +162,8 @@ def test_alignment(lib):
     assert lib.rsa_attn_omitted(ctypes.byref(p), b.ptr, b.ptr, b.ptr, b.ptr, b.ptr, None, mis, b.ptr,
                                 b.ptr, 1 << 30, None) == ALIGN
     assert lib.rsa_attn_merge(ctypes.byref(p), b.ptr, b.ptr, mis, b.ptr, None) == ALIGN
+    assert lib.rsa_block_sparse_attn_corrected(ctypes.byref(p), b.ptr, b.ptr, b.ptr, b.ptr, b.ptr, mis, b.ptr,
+                                               b.ptr, b.ptr, b.ptr, 1 << 30, None) == ALIGN
     assert b.untouched()
 
 

@@ -11,6 +11,9 @@ by the fresh sparse statistics.
 * rsa_attn_merge of the GPU's own sparse and omitted parts against dense
   attention (the oracle's merge identity), and against the oracle's merge of
   the same parts;
+* rsa_block_sparse_attn_corrected (the sparse pass joined with the cached
+  part inside the attention kernel) against dense attention, against the
+  GPU's sparse pass followed by rsa_attn_merge, and in place;
 * heads switched off by head_active keep their cached rows bit for bit;
 * the mask cache with the correction on, over a drifting trajectory (q, k and
   v walk), against the oracle's corrected_trajectory.
@@ -102,6 +105,8 @@ class Case:
         self.parts = (host(self.s_out), host(self.s_lse), host(self.o_out), host(self.o_lse))
         self.m_out, self.m_lse = self.s_out.clone(), self.s_lse.clone()
         R.attn_merge(self.m_out, self.m_lse, self.o_out, self.o_lse, self.p)
+        self.c_out, self.c_lse = R.block_sparse_attn_corrected(self.q, self.k, self.v, self.counts, self.idx,
+                                                               self.o_out, self.o_lse, self.p)
         torch.cuda.synchronize()
 
 
@@ -168,6 +173,56 @@ def test_merge_matches_oracle_merge_of_same_parts(name):
     assert (np.isneginf(lse) == np.isneginf(l_or)).all()
     live = np.isfinite(l_or)
     assert np.abs(lse[live] - l_or[live]).max() <= 2e-6 * max(1.0, np.abs(l_or[live]).max())
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_corrected_attention_is_dense(name):
+    """Sparse pass and cached omitted part joined in the attention kernel: on
+    the inputs the part was cached from, the union of the two key sets is every
+    key, so the result is dense attention."""
+    c = case(name)
+    wl = c.wl
+    tol_l2, tol_abs, tol_lse = ATTN_TOL[wl.dtype]
+    out, lse = host(c.c_out), host(c.c_lse)
+    full = [list(range(wl.nblocks))] * wl.nblocks
+    for h in range(wl.heads):
+        o_or, l_or = O.block_sparse_attention(c.q64[h], c.k64[h], c.v64[h], wl.block, full)
+        e = (rel_l2(out[h], o_or), np.abs(out[h] - o_or).max(), np.abs(lse[h] - l_or).max())
+        say(f"[gpu] corrected vs dense {name} h={h}: rel-l2 {e[0]:.2e} max-abs {e[1]:.2e} lse {e[2]:.2e}")
+        assert e[0] <= tol_l2 and e[1] <= tol_abs and e[2] <= tol_lse
+
+
+@pytest.mark.parametrize("name", sorted(CASES))
+def test_corrected_matches_sparse_then_merge(name):
+    """One pass against two: the fused join takes the sparse output before its
+    rounding to the output type.  bf16 rounds to nearest with an 8-bit
+    significand (error at most 2^-8 relative), so the two differ by at most
+    that rounding of the sparse part plus one rounding of each result; fp32
+    by a few fp32 roundings.  The lse is the same."""
+    c = case(name)
+    out, m_out = host(c.c_out), host(c.m_out)
+    so = np.abs(host(c.s_out)).max(axis=-1, keepdims=True)
+    oo = np.abs(host(c.o_out)).max(axis=-1, keepdims=True)
+    if c.wl.dtype == "bf16":
+        bound = 2.0 ** -7 * np.maximum(np.abs(out), np.abs(m_out)) + 2.0 ** -8 * so + 1e-6 * oo
+    else:
+        bound = 1e-6 * (so + oo)
+    excess = np.abs(out - m_out) - bound
+    say(f"[gpu] corrected vs sparse + merge {name}: worst excess over the bound {excess.max():.2e}")
+    assert (excess <= 0).all()
+    lse, m_lse = host(c.c_lse), host(c.m_lse)
+    assert (np.isneginf(lse) == np.isneginf(m_lse)).all()
+    live = np.isfinite(m_lse)
+    assert np.abs(lse[live] - m_lse[live]).max() <= 2e-6 * max(1.0, np.abs(m_lse[live]).max())
+
+
+def test_corrected_in_place():
+    """out and lse may be the cached part itself: the same result, bit for bit."""
+    c = case("bf16_d128_b64")
+    out, lse = c.o_out.clone(), c.o_lse.clone()
+    R.block_sparse_attn_corrected(c.q, c.k, c.v, c.counts, c.idx, out, lse, c.p, out=out, lse=lse)
+    torch.cuda.synchronize()
+    assert torch.equal(out, c.c_out) and torch.equal(lse, c.c_lse)
 
 
 def test_merge_with_empty_parts_is_exact():
