@@ -576,24 +576,24 @@ __global__ __launch_bounds__(2 * B, NBUF == 3 ? 3 : 2) void attn_bf16_kernel(
         if constexpr (kTable) mask_tail(jj, sprev);
         mprev = rowmax(sprev);
       } else {
+        // the single-block step with each half skipped where this wave's
+        // block did not select the sub-tile (wave-uniform branches)
         const bool mc = member(jj);
         if (pvalid) rescale(mprev);
         wait_vm<(NBUF - 3) * kPer>();
         barrier_lds();
         issue(jj + NBUF - 2, fill);
-        if (mc && pvalid) {
-          f32x16 scur[S::kKT];
+        f32x16 scur[S::kKT];
+        if (mc) {
           qk(kslot, scur);
-          pv(sprev, vslot);
+        } else {
 #pragma unroll
-          for (int t = 0; t < S::kKT; ++t) sprev[t] = scur[t];
-          mprev = rowmax(sprev);
-        } else if (mc) {
-          qk(kslot, sprev);
-          mprev = rowmax(sprev);
-        } else if (pvalid) {
-          pv(sprev, vslot);
+          for (int t = 0; t < S::kKT; ++t) scur[t] = f32x16{} - INFINITY;
         }
+        if (pvalid) pv(sprev, vslot);
+#pragma unroll
+        for (int t = 0; t < S::kKT; ++t) sprev[t] = scur[t];
+        if (mc) mprev = rowmax(sprev);
         pvalid = mc;
       }
     };
@@ -809,8 +809,8 @@ hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const v
   if (e != hipSuccess) return e;
   if (p.dtype == 0) {
     // Single blocks: a ring of three 32-key sub-tiles, three workgroups per
-    // CU.  Pairs keep four slots and two workgroups per CU: their
-    // membership masks do not fit the three-wave register budget.
+    // CU.  Pairs keep four slots and two workgroups per CU: at the
+    // three-wave register budget their skip logic spills.
     constexpr int kKs = RSA_ATTN_KS, kNbuf = kPairs ? 4 : RSA_ATTN_NBUF;
     constexpr int kRows = 128;  // query rows per workgroup (a block, or a pair of 64-token blocks)
     using S = AttnShape<D, kRows, kKs, kNbuf>;
