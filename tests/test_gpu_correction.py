@@ -16,7 +16,8 @@ by the fresh sparse statistics.
   GPU's sparse pass followed by rsa_attn_merge, and in place;
 * heads switched off by head_active keep their cached rows bit for bit;
 * the mask cache with the correction on, over a drifting trajectory (q, k and
-  v walk), against the oracle's corrected_trajectory.
+  v walk), against the oracle's corrected_trajectory, and after a Turbo
+  re-selection (every head's omitted part recomputed).
 """
 import sys
 
@@ -315,6 +316,30 @@ def test_corrected_trajectory_against_oracle():
             assert e[0] <= tol_l2 and e[1] <= tol_abs and e[2] <= tol_lse
     say(f"[gpu] corrected trajectory refreshes per head: {refreshes.tolist()}")
     assert (refreshes > 1).any() and (refreshes < 5).any()   # heads refresh at different steps
+
+
+def test_turbo_then_corrected_step_is_dense():
+    """A Turbo re-selection changes every head's list, so the next corrected
+    step recomputes every head's omitted part: on unchanged inputs (no head
+    refreshes) the corrected output is still dense attention."""
+    c = case("bf16_d64_b64")
+    wl = c.wl
+    cache = R.MaskCache(c.p, torch.from_numpy(wl.top_p_array()).to(DEV), 0.05, correction=True)
+    cache.step(c.q, c.k, c.v)
+    before = cache.counts.clone()
+    cache.turbo(torch.full((wl.heads,), 0.6, dtype=torch.float32, device=DEV))
+    out, lse = cache.step(c.q, c.k, c.v)
+    torch.cuda.synchronize()
+    assert int(cache.refresh.sum().item()) == 0                      # nothing refreshed by drift
+    assert (cache.counts <= before).all() and (cache.counts < before).any()  # Turbo shrank the lists
+    tol_l2, tol_abs, tol_lse = ATTN_TOL["bf16"]
+    o, l = host(out), host(lse)
+    full = [list(range(wl.nblocks))] * wl.nblocks
+    for h in range(wl.heads):
+        o_or, l_or = O.block_sparse_attention(c.q64[h], c.k64[h], c.v64[h], wl.block, full)
+        e = (rel_l2(o[h], o_or), np.abs(o[h] - o_or).max(), np.abs(l[h] - l_or).max())
+        say(f"[gpu] turbo + corrected h={h}: rel-l2 {e[0]:.2e} max-abs {e[1]:.2e} lse {e[2]:.2e}")
+        assert e[0] <= tol_l2 and e[1] <= tol_abs and e[2] <= tol_lse
 
 
 def _snapshots(steps64, gpu, s):
