@@ -918,9 +918,13 @@ __global__ __launch_bounds__(256) void cl_scan_kernel(const int* __restrict__ si
   }
 }
 
-// One workgroup per (cluster, head): K rows into the padded layout and V^T
-// columns (vt_pos order inside every 16 keys, as the attention kernel reads
-// them), 32 keys at a time through an LDS tile.
+// One workgroup per (32-key sub-tile of the padded layout, head): K rows
+// into the padded layout and V^T columns (vt_pos order inside every 16 keys,
+// as the attention kernel reads them) through an LDS tile.  The sub-tile's
+// cluster is the last j with pstart[j] <= its first key (an empty cluster
+// shares its start with the next one); sub-tiles past the last cluster are
+// left alone (no table entry names them).  Per sub-tile rather than per
+// cluster, so the largest clusters do not set the time.
 template <int D>
 __global__ __launch_bounds__(256) void cl_gather_bf16_kernel(const uint16_t* __restrict__ k,
                                                              const uint16_t* __restrict__ v,
@@ -931,42 +935,48 @@ __global__ __launch_bounds__(256) void cl_gather_bf16_kernel(const uint16_t* __r
                                                              uint16_t* __restrict__ kp, uint16_t* __restrict__ vtp,
                                                              int N, int NB, int Np) {
   __shared__ uint16_t tile[32][D + 2];
-  const int j = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
-  const size_t row = static_cast<size_t>(h) * NB + j;
+  const int t = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  const int key0 = 32 * t;
+  const int* ps_h = pstart + static_cast<size_t>(h) * NB;
+  // last j with ps_h[j] <= key0 (ps_h is non-decreasing, ps_h[0] = 0)
+  int lo = 0, hi = NB - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (ps_h[mid] <= key0) lo = mid;
+    else hi = mid - 1;
+  }
+  const size_t row = static_cast<size_t>(h) * NB + lo;
   const int n = sizes[row];
-  if (n <= 0) return;
-  const int ps = pstart[row];
+  const int s0 = key0 - ps_h[lo];  // first key of the sub-tile inside the cluster
+  if (n <= 0 || s0 >= ((n + 31) & ~31)) return;
   const int* ord = order + static_cast<size_t>(h) * N + ostart[row];
-  for (int s0 = 0; s0 < n; s0 += 32) {
-    __syncthreads();
-    for (int c = tid; c < 32 * D / 8; c += 256) {
-      const int r = c / (D / 8), c8 = c % (D / 8);
-      const int tok = s0 + r < n ? ord[s0 + r] : -1;
-      u32x4 kx = u32x4{0, 0, 0, 0}, vx = u32x4{0, 0, 0, 0};
-      if (static_cast<unsigned>(tok) < static_cast<unsigned>(N)) {  // padding, or an invalid id: zeros
-        const size_t g = (static_cast<size_t>(h) * N + tok) * D + c8 * 8;
-        kx = *reinterpret_cast<const u32x4*>(k + g);
-        vx = *reinterpret_cast<const u32x4*>(v + g);
-      }
-      *reinterpret_cast<u32x4*>(kp + (static_cast<size_t>(h) * Np + ps + s0 + r) * D + c8 * 8) = kx;
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        tile[r][c8 * 8 + 2 * e] = static_cast<uint16_t>(vx[e] & 0xffffu);
-        tile[r][c8 * 8 + 2 * e + 1] = static_cast<uint16_t>(vx[e] >> 16);
-      }
+  for (int c = tid; c < 32 * D / 8; c += 256) {
+    const int r = c / (D / 8), c8 = c % (D / 8);
+    const int tok = s0 + r < n ? ord[s0 + r] : -1;
+    u32x4 kx = u32x4{0, 0, 0, 0}, vx = u32x4{0, 0, 0, 0};
+    if (static_cast<unsigned>(tok) < static_cast<unsigned>(N)) {  // padding, or an invalid id: zeros
+      const size_t g = (static_cast<size_t>(h) * N + tok) * D + c8 * 8;
+      kx = *reinterpret_cast<const u32x4*>(k + g);
+      vx = *reinterpret_cast<const u32x4*>(v + g);
     }
-    __syncthreads();
-    for (int c = tid; c < D * 4; c += 256) {
-      const int d = c / 4, p8 = c % 4;
-      u32x4 o;
+    *reinterpret_cast<u32x4*>(kp + (static_cast<size_t>(h) * Np + key0 + r) * D + c8 * 8) = kx;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const uint32_t lo = tile[vt_pos(8 * p8 + 2 * e)][d];
-        const uint32_t hi = tile[vt_pos(8 * p8 + 2 * e + 1)][d];
-        o[e] = lo | (hi << 16);
-      }
-      *reinterpret_cast<u32x4*>(vtp + (static_cast<size_t>(h) * D + d) * Np + ps + s0 + 8 * p8) = o;
+    for (int e = 0; e < 4; ++e) {
+      tile[r][c8 * 8 + 2 * e] = static_cast<uint16_t>(vx[e] & 0xffffu);
+      tile[r][c8 * 8 + 2 * e + 1] = static_cast<uint16_t>(vx[e] >> 16);
     }
+  }
+  __syncthreads();
+  for (int c = tid; c < D * 4; c += 256) {
+    const int d = c / 4, p8 = c % 4;
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const uint32_t lo16 = tile[vt_pos(8 * p8 + 2 * e)][d];
+      const uint32_t hi16 = tile[vt_pos(8 * p8 + 2 * e + 1)][d];
+      o[e] = lo16 | (hi16 << 16);
+    }
+    *reinterpret_cast<u32x4*>(vtp + (static_cast<size_t>(h) * D + d) * Np + key0 + 8 * p8) = o;
   }
 }
 
@@ -1105,7 +1115,7 @@ hipError_t launch_cluster_attn_t(const Problem& p, const void* q, const void* k,
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.dtype == 0)
-    hipLaunchKernelGGL((cl_gather_bf16_kernel<D>), dim3(p.nb, p.heads), dim3(256), 0, stream,
+    hipLaunchKernelGGL((cl_gather_bf16_kernel<D>), dim3(w.stride, p.heads), dim3(256), 0, stream,
                        static_cast<const uint16_t*>(k), static_cast<const uint16_t*>(v), csize, order, pstart,
                        ostart, reinterpret_cast<uint16_t*>(base + w.kp_off),
                        reinterpret_cast<uint16_t*>(base + w.vp_off), p.tokens, p.nb, w.Np);
