@@ -277,7 +277,7 @@ def retrieval(args):
         "mode": "retrieval",
         "metric": "dense attention mass captured by the selected key blocks (mean over query blocks)",
         "workload": wl.name, "heads": wl.heads, "tokens": wl.tokens, "block": wl.block,
-        "top_p": float(inp.top_p[0]),
+        "top_p": round(float(inp.top_p[0]), 6),
         "data": "synthetic (seeded smooth 3-D field + noise; no weights)",
         "equal_density": {
             "density": round(float(kk.sum() / (wl.heads * nb * nb)), 4),
@@ -382,7 +382,7 @@ def correction(args):
         "mode": "correction",
         "metric": "relative L2 error against dense attention, mean over heads (lower is better)",
         "workload": wl.name, "heads": wl.heads, "tokens": wl.tokens, "block": wl.block,
-        "top_p": float(inp.top_p[0]), "drift_threshold": wl.drift_threshold,
+        "top_p": round(float(inp.top_p[0]), 6), "drift_threshold": wl.drift_threshold,
         "data": "synthetic (seeded smooth 3-D field + noise; q, k, v random walk per step; no weights)",
         "steps": per_step,
         "refreshes_per_head": {"min": int(refresh_total.min()), "max": int(refresh_total.max()),
@@ -610,7 +610,7 @@ def main():
         "data": "synthetic (seeded smooth 3-D field + noise, Wan2.1-14B 720p latent shape; no weights)",
         "config": {
             "workload": wl.name, "heads": wl.heads, "grid": list(wl.grid), "tokens": wl.tokens,
-            "head_dim": wl.head_dim, "block": wl.block, "top_p": float(inp.top_p[0]),
+            "head_dim": wl.head_dim, "block": wl.block, "top_p": round(float(inp.top_p[0]), 6),
             "parallelism": "single GPU",
         },
         "attn_ms_per_call": round(per["attn"], 3),
