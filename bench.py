@@ -610,7 +610,9 @@ def main():
         "data": "synthetic (seeded smooth 3-D field + noise, Wan2.1-14B 720p latent shape; no weights)",
         "config": {
             "workload": wl.name, "heads": wl.heads, "grid": list(wl.grid), "tokens": wl.tokens,
-            "head_dim": wl.head_dim, "block": wl.block, "top_p": round(float(inp.top_p[0]), 6),
+            "head_dim": wl.head_dim, "block": wl.block,
+            # one value, or the per-head pattern (head h takes entry h mod its length)
+            "top_p": wl.top_p[0] if len(set(wl.top_p)) == 1 else list(wl.top_p),
             "parallelism": "single GPU",
         },
         "attn_ms_per_call": round(per["attn"], 3),
