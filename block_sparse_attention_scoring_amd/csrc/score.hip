@@ -10,7 +10,8 @@
 //   split: per head one power-of-two factor t_h brings max |Kbar| into
 //          [2^13, 2^14); Kbar*t_h = hi + lo with hi, lo fp16.  hi+lo holds
 //          22 significant bits, so the logits below are fp32-faithful.
-//   score: one workgroup per (head, query block).  Each query row is scaled
+//   score: one four-wave workgroup per (head, query block of 128 tokens, or
+//          pair of 64-token blocks).  Each query row is scaled
 //          by its own power of two and held as fp16 in registers (exact for
 //          bf16 input; fp32 input is split into two fp16 terms); the split
 //          pooled keys stream through an LDS ring.  The logits run on the
@@ -180,7 +181,9 @@ __device__ __forceinline__ float reduce_scatter_32(const float (&v)[16], int col
 // wave keeps its rows in registers, scaled by the row's own power of two and
 // held as fp16 (exact for bf16 input; fp32 input adds a second fp16 term).
 // The split pooled keys stream in chunks of 32 key blocks (hi and lo tiles)
-// into a ring of NBUF LDS slots with buffer loads, shared by all waves.
+// into a ring of NBUF LDS slots with buffer loads, shared by all waves; with
+// three slots (48 KB) three workgroups share a CU and the register budget is
+// capped to match.
 // Both passes form one walk of 2 x NBp/32 chunk steps, so the prefetch runs
 // on across the pass boundary:
 //   pass 1 (chunk steps 0..nc-1): logits S^T = Kbar Q^T (hi and lo terms in
