@@ -631,6 +631,40 @@ def test_kmeans_query_metric_is_euclidean_on_transformed_keys():
     assert (O.assign(k, cents, g)[0] == sk_l).all()
 
 
+def test_cluster_keys_is_kmeans_in_the_query_metric_then_stable_order():
+    """The whole clustering of a head, pinned without the oracle's own metric
+    helpers: a QR factor of the queries gives R with R^T R = Q^T Q, so the
+    query metric is Euclidean distance between keys mapped by x -> x R^T /
+    sqrt(N), and scikit-learn's Lloyd from the mapped contiguous block means
+    (taken by reshaping, not by the oracle's pooling) gives the centroids.
+    Sizes, the means of the returned clusters and the stable order are
+    checked by brute force.  The queries see mostly two coordinates, so a
+    metric built from the keys instead of the queries clusters differently."""
+    rng = np.random.default_rng(131)
+    n, d, b = 180, 6, 20
+    q = rng.standard_normal((400, d)) * np.array([3.0, 0.2, 2.0, 0.1, 0.1, 0.1])
+    k = _clustered_keys(n, d, n // b, 132, spread=1.5)
+    R = np.linalg.qr(q, mode="r") / np.sqrt(q.shape[0])
+    start = k.reshape(n // b, b, d).mean(axis=1)
+    for iters in (1, 3):
+        labels, cents, sizes, order = O.cluster_keys(q, k, b, iters)
+        sk_c, _ = _sk_lloyd(k @ R.T, start @ R.T, iters)
+        np.testing.assert_allclose(cents @ R.T, sk_c, atol=1e-10)
+        assert (sizes == np.bincount(labels, minlength=n // b)).all()
+        for j in np.flatnonzero(sizes):
+            np.testing.assert_allclose(cents[j], k[labels == j].mean(axis=0), atol=1e-12)
+        want = np.concatenate([np.flatnonzero(labels == j) for j in range(n // b)])
+        assert (order == want).all()
+        # the labels are the nearest centroids of the previous iteration's means
+        prev = start if iters == 1 else _sk_lloyd(k @ R.T, start @ R.T, iters - 1)[0]
+        dist = (((k @ R.T)[:, None, :] - prev[None, :, :] if iters > 1 else
+                 (k @ R.T)[:, None, :] - (start @ R.T)[None, :, :]) ** 2).sum(-1)
+        assert (labels == np.argmin(dist, axis=1)).all()
+    # the same pipeline in the keys' own metric gives other clusters
+    wrong, _, _ = O.kmeans(k, k.T @ k / n, b, 3)
+    assert (wrong != O.cluster_keys(q, k, b, 3)[0]).any()
+
+
 def test_query_aware_clusters_group_equal_scores():
     """Queries that only see coordinate 0: keys differ there by sign and
     elsewhere by large noise.  The query metric splits the keys by sign, so
