@@ -1,10 +1,10 @@
 // Per-head query-key drift and refresh flags (gfx950).
 //
 // HEART (Exploiting Head Heterogeneity in Sparse Attention for Video
-// Diffusion), Abstract: Temporal Mask Reuse keeps a head's cached mask while
-// a lightweight per-head query-key drift signal stays small and refreshes it
-// when the drift exceeds a prescribed threshold; HASTE, Abstract, skips mask
-// prediction on the same signal.  The signal is the relative Frobenius change
+// Diffusion), Abstract (Temporal Mask Reuse): a head keeps its cached mask
+// until a cheap measure of how far its queries and keys have moved rises above
+// a threshold tau, and only then is the mask recomputed; HASTE, Abstract, uses
+// the same kind of measure to decide when mask prediction can be skipped.  The signal is the relative Frobenius change
 // of the head's stacked (Q, K) since its last refresh:
 //
 //   d_h = sqrt(|Q - Qref|^2 + |K - Kref|^2) / sqrt(|Qref|^2 + |Kref|^2).

@@ -178,9 +178,9 @@ rsa_status rsa_select_topp(const rsa_problem* p, const float* scores, const floa
                            float* density, void* ws, size_t ws_bytes, hipStream_t stream);
 
 /*
- * Per-head query-key drift and refresh flags (HEART, Abstract: refresh a
- * cached mask only when the head's drift exceeds a prescribed threshold;
- * HASTE, Abstract: skip mask prediction from query-key drift).
+ * Per-head query-key drift and refresh flags (HEART, Abstract: a head's
+ * cached mask is recomputed only once its drift is above tau; HASTE,
+ * Abstract: the drift decides when mask prediction may be skipped).
  *
  *   drift[h] = sqrt(|Q_h - Qref_h|^2 + |K_h - Kref_h|^2) / sqrt(|Qref_h|^2 + |Kref_h|^2)
  *   refresh[h] = drift[h] > threshold  (strict; an all-zero snapshot gives

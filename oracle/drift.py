@@ -1,9 +1,9 @@
 """Per-head query-key drift and the refresh rule, fp64 (oracle; test infrastructure only).
 
-HEART, Abstract: Temporal Mask Reuse keeps a cached mask while a lightweight
-per-head query-key drift signal stays small, and refreshes it only when the
-drift exceeds a prescribed threshold.  HASTE, Abstract: mask prediction is
-skipped based on query-key drift.
+HEART, Abstract (Temporal Mask Reuse): a head's cached mask stays in use
+until a cheap per-head measure of how far its queries and keys have moved
+rises above a threshold tau; then the mask is recomputed.  HASTE, Abstract:
+the same kind of measure decides when mask prediction can be skipped.
 
 Reading (the pages give no formula): the relative Frobenius change of the
 head's stacked queries and keys since the snapshot taken when its mask was
