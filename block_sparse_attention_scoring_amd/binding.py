@@ -114,6 +114,54 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t: Optional[torch.Tensor], name: str, dtype: torch.dtype, shape, optional: bool = False):
+    """Reject, before any library call, a tensor the C entry points would
+    misread: they take bare device pointers to dense row-major arrays."""
+    if t is None:
+        if optional:
+            return
+        raise ValueError(f"{name} is required")
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor, got {type(t).__name__}")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if tuple(t.shape) != tuple(int(x) for x in shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous (row-major); call .contiguous() first")
+
+
+def _gpu(**tensors):
+    """Every given tensor (None allowed) must live on the GPU; checked after
+    the dtype/shape/layout checks of the same call."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a GPU tensor, got device {t.device}")
+
+
+def _io_dtype(p: "Problem") -> torch.dtype:
+    return torch.bfloat16 if p.dtype == RSA_BF16 else torch.float32
+
+
+def _need_qkv(p: "Problem", **tensors):
+    dt, shp = _io_dtype(p), (p.heads, p.tokens, p.head_dim)
+    for name, t in tensors.items():
+        _need(t, name, dt, shp)
+
+
+def _need_lists(p: "Problem", counts, block_idx):
+    nb = p.nblocks
+    _need(counts, "counts", torch.int32, (p.heads, nb))
+    _need(block_idx, "block_idx", torch.int32, (p.heads, nb, nb))
+
+
+def _need_workspace(ws: Optional[torch.Tensor]):
+    if ws is None:
+        return
+    if not isinstance(ws, torch.Tensor) or ws.dtype != torch.uint8 or ws.dim() != 1 or not ws.is_contiguous():
+        raise ValueError("workspace must be a contiguous 1-D uint8 tensor")
+
+
 def _stream(t: torch.Tensor):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
@@ -148,6 +196,11 @@ def _workspace(p: Problem, op: int, device, ws: Optional[torch.Tensor]):
 
 def score_blocks(q, k, p: Problem, head_active=None, out=None, workspace=None):
     """PARK block scores [heads, NB, NB] fp32 (rsa_score_blocks)."""
+    _need_qkv(p, q=q, k=k)
+    _need(head_active, "head_active", torch.uint8, (p.heads,), optional=True)
+    _need(out, "out", torch.float32, (p.heads, p.nblocks, p.nblocks), optional=True)
+    _need_workspace(workspace)
+    _gpu(q=q, k=k, head_active=head_active, out=out, workspace=workspace)
     nb = p.nblocks
     if out is None:
         out = torch.empty((p.heads, nb, nb), dtype=torch.float32, device=q.device)
@@ -160,6 +213,15 @@ def score_blocks(q, k, p: Problem, head_active=None, out=None, workspace=None):
 def select_topp(scores, top_p, p: Problem, max_blocks: int = 0, head_active=None, mask=None,
                 counts=None, block_idx=None, density=None, want_density: bool = True):
     """Top-p selection -> (mask u8, counts i32, block_idx i32, density fp32 or None)."""
+    nbq = p.nblocks
+    _need(scores, "scores", torch.float32, (p.heads, nbq, nbq))
+    _need(top_p, "top_p", torch.float32, (p.heads,))
+    _need(head_active, "head_active", torch.uint8, (p.heads,), optional=True)
+    _need(mask, "mask", torch.uint8, (p.heads, nbq, nbq), optional=True)
+    _need(counts, "counts", torch.int32, (p.heads, nbq), optional=True)
+    _need(block_idx, "block_idx", torch.int32, (p.heads, nbq, nbq), optional=True)
+    _need(density, "density", torch.float32, (p.heads,), optional=True)
+    _gpu(scores=scores, top_p=top_p, head_active=head_active, mask=mask, counts=counts, block_idx=block_idx, density=density)
     nb = p.nblocks
     dev = scores.device
     if mask is None:
@@ -179,6 +241,11 @@ def select_topp(scores, top_p, p: Problem, max_blocks: int = 0, head_active=None
 def mask_drift(q, k, q_ref, k_ref, p: Problem, threshold: float, update_ref: bool = True,
                drift=None, refresh=None, workspace=None):
     """Per-head drift and refresh flags -> (drift fp32 [H], refresh u8 [H])."""
+    _need_qkv(p, q=q, k=k, q_ref=q_ref, k_ref=k_ref)
+    _need(drift, "drift", torch.float32, (p.heads,), optional=True)
+    _need(refresh, "refresh", torch.uint8, (p.heads,), optional=True)
+    _need_workspace(workspace)
+    _gpu(q=q, k=k, q_ref=q_ref, k_ref=k_ref, drift=drift, refresh=refresh, workspace=workspace)
     if drift is None:
         drift = torch.empty((p.heads,), dtype=torch.float32, device=q.device)
     if refresh is None:
@@ -193,6 +260,12 @@ def mask_drift(q, k, q_ref, k_ref, p: Problem, threshold: float, update_ref: boo
 def block_sparse_attn(q, k, v, counts, block_idx, p: Problem, out=None, lse=None,
                       want_lse: bool = True, workspace=None):
     """Attention over the listed key blocks -> (out like q, lse fp32 [H, N] or None)."""
+    _need_qkv(p, q=q, k=k, v=v)
+    _need_lists(p, counts, block_idx)
+    _need(out, "out", _io_dtype(p), (p.heads, p.tokens, p.head_dim), optional=True)
+    _need(lse, "lse", torch.float32, (p.heads, p.tokens), optional=True)
+    _need_workspace(workspace)
+    _gpu(q=q, k=k, v=v, counts=counts, block_idx=block_idx, out=out, lse=lse, workspace=workspace)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
@@ -206,6 +279,9 @@ def block_sparse_attn(q, k, v, counts, block_idx, p: Problem, out=None, lse=None
 
 def dense_block_mass(q, k, p: Problem, out=None):
     """Dense attention mass of each query block per key block [heads, NB, NB] fp32."""
+    _need_qkv(p, q=q, k=k)
+    _need(out, "out", torch.float32, (p.heads, p.nblocks, p.nblocks), optional=True)
+    _gpu(q=q, k=k, out=out)
     nb = p.nblocks
     if out is None:
         out = torch.empty((p.heads, nb, nb), dtype=torch.float32, device=q.device)
@@ -216,6 +292,10 @@ def dense_block_mass(q, k, p: Problem, out=None):
 
 def score_blocks_pooled(q, k, p: Problem, out=None, workspace=None):
     """Query-pooled comparison scores [heads, NB, NB] fp32 (rsa_score_blocks_pooled)."""
+    _need_qkv(p, q=q, k=k)
+    _need(out, "out", torch.float32, (p.heads, p.nblocks, p.nblocks), optional=True)
+    _need_workspace(workspace)
+    _gpu(q=q, k=k, out=out, workspace=workspace)
     nb = p.nblocks
     if out is None:
         out = torch.empty((p.heads, nb, nb), dtype=torch.float32, device=q.device)
@@ -231,6 +311,13 @@ def attn_omitted(q, k, v, counts, block_idx, p: Problem, head_active=None, out=N
 
     Heads with head_active[h] == 0 keep what ``out``/``lse`` held (pass the
     cache's buffers to refresh only some heads)."""
+    _need_qkv(p, q=q, k=k, v=v)
+    _need_lists(p, counts, block_idx)
+    _need(head_active, "head_active", torch.uint8, (p.heads,), optional=True)
+    _need(out, "out", _io_dtype(p), (p.heads, p.tokens, p.head_dim), optional=True)
+    _need(lse, "lse", torch.float32, (p.heads, p.tokens), optional=True)
+    _need_workspace(workspace)
+    _gpu(q=q, k=k, v=v, counts=counts, block_idx=block_idx, head_active=head_active, out=out, lse=lse, workspace=workspace)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -244,6 +331,10 @@ def attn_omitted(q, k, v, counts, block_idx, p: Problem, head_active=None, out=N
 
 def attn_merge(out, lse, part_out, part_lse, p: Problem):
     """In place: (out, lse) <- attention over the union of two disjoint key sets."""
+    _need_qkv(p, out=out, part_out=part_out)
+    _need(lse, "lse", torch.float32, (p.heads, p.tokens))
+    _need(part_lse, "part_lse", torch.float32, (p.heads, p.tokens))
+    _gpu(out=out, part_out=part_out, lse=lse, part_lse=part_lse)
     _check(lib().rsa_attn_merge(ctypes.byref(p), _ptr(out), _ptr(lse), _ptr(part_out), _ptr(part_lse),
                                 _stream(out)), "rsa_attn_merge")
     return out, lse
@@ -254,6 +345,13 @@ def block_sparse_attn_corrected(q, k, v, counts, block_idx, part_out, part_lse, 
     """Sparse attention over the lists joined with a cached complementary part
     in one pass -> (out like q, lse fp32 [H, N]) (rsa_block_sparse_attn_corrected).
     ``out``/``lse`` may be ``part_out``/``part_lse`` (in place)."""
+    _need_qkv(p, q=q, k=k, v=v, part_out=part_out)
+    _need_lists(p, counts, block_idx)
+    _need(part_lse, "part_lse", torch.float32, (p.heads, p.tokens))
+    _need(out, "out", _io_dtype(p), (p.heads, p.tokens, p.head_dim), optional=True)
+    _need(lse, "lse", torch.float32, (p.heads, p.tokens), optional=True)
+    _need_workspace(workspace)
+    _gpu(q=q, k=k, v=v, part_out=part_out, counts=counts, block_idx=block_idx, part_lse=part_lse, out=out, lse=lse, workspace=workspace)
     if out is None:
         out = torch.empty_like(q)
     if lse is None:
@@ -268,6 +366,10 @@ def block_sparse_attn_corrected(q, k, v, counts, block_idx, part_out, part_lse, 
 
 def query_gram(q, p: Problem, out=None, workspace=None):
     """Gram matrix of the current queries, [heads, head_dim, head_dim] fp32 (rsa_query_gram)."""
+    _need_qkv(p, q=q)
+    _need(out, "out", torch.float32, (p.heads, p.head_dim, p.head_dim), optional=True)
+    _need_workspace(workspace)
+    _gpu(q=q, out=out, workspace=workspace)
     if out is None:
         out = torch.empty((p.heads, p.head_dim, p.head_dim), dtype=torch.float32, device=q.device)
     ws, wsb = _workspace(p, OP_GRAM, q.device, workspace)
@@ -279,6 +381,14 @@ def kmeans(k, gram, p: Problem, iters: int, init: bool = True, centroids=None, l
            order=None, workspace=None):
     """Lloyd k-means of the keys in the metric of ``gram`` (rsa_kmeans)
     -> (centroids fp32 [H, NB, D], labels i32 [H, N], sizes i32 [H, NB], order i32 [H, N])."""
+    _need_qkv(p, k=k)
+    _need(gram, "gram", torch.float32, (p.heads, p.head_dim, p.head_dim))
+    _need(centroids, "centroids", torch.float32, (p.heads, p.nblocks, p.head_dim), optional=True)
+    _need(labels, "labels", torch.int32, (p.heads, p.tokens), optional=True)
+    _need(sizes, "sizes", torch.int32, (p.heads, p.nblocks), optional=True)
+    _need(order, "order", torch.int32, (p.heads, p.tokens), optional=True)
+    _need_workspace(workspace)
+    _gpu(k=k, gram=gram, centroids=centroids, labels=labels, sizes=sizes, order=order, workspace=workspace)
     nb, dev = p.nblocks, k.device
     if centroids is None:
         if not init:
@@ -298,6 +408,12 @@ def kmeans(k, gram, p: Problem, iters: int, init: bool = True, centroids=None, l
 
 def score_clusters(q, centroids, sizes, p: Problem, out=None, workspace=None):
     """PARK scores with clusters as key blocks, [heads, NB, NB] fp32 (rsa_score_clusters)."""
+    _need_qkv(p, q=q)
+    _need(centroids, "centroids", torch.float32, (p.heads, p.nblocks, p.head_dim))
+    _need(sizes, "sizes", torch.int32, (p.heads, p.nblocks))
+    _need(out, "out", torch.float32, (p.heads, p.nblocks, p.nblocks), optional=True)
+    _need_workspace(workspace)
+    _gpu(q=q, centroids=centroids, sizes=sizes, out=out, workspace=workspace)
     nb = p.nblocks
     if out is None:
         out = torch.empty((p.heads, nb, nb), dtype=torch.float32, device=q.device)
@@ -310,6 +426,14 @@ def score_clusters(q, centroids, sizes, p: Problem, out=None, workspace=None):
 def cluster_attn(q, k, v, sizes, order, counts, block_idx, p: Problem, out=None, lse=None, want_lse: bool = True,
                  workspace=None):
     """Attention over the listed clusters' keys -> (out like q, lse fp32 [H, N] or None) (rsa_cluster_attn)."""
+    _need_qkv(p, q=q, k=k, v=v)
+    _need(sizes, "sizes", torch.int32, (p.heads, p.nblocks))
+    _need(order, "order", torch.int32, (p.heads, p.tokens))
+    _need_lists(p, counts, block_idx)
+    _need(out, "out", _io_dtype(p), (p.heads, p.tokens, p.head_dim), optional=True)
+    _need(lse, "lse", torch.float32, (p.heads, p.tokens), optional=True)
+    _need_workspace(workspace)
+    _gpu(q=q, k=k, v=v, sizes=sizes, order=order, counts=counts, block_idx=block_idx, out=out, lse=lse, workspace=workspace)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
