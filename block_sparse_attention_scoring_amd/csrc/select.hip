@@ -11,9 +11,11 @@
 // the blocks by score descending and, for equal scores, by index ascending.
 // Each lane holds E consecutive keys of the padded row (MP = 64 E >= NB) in
 // registers; the bitonic network runs its strides below E inside the lane
-// and the others between lanes (shuffles).  The sorted scores are summed in
-// fp64 (in-lane, then a wave scan); the first rank whose running mass
-// reaches p[h] fixes k*, and the key at rank k* - 1 is the threshold: block
+// and the others between lanes (shuffles).  The running mass is the fp64 sum
+// of the sorted scores in rank order; it is formed in-lane plus a wave scan,
+// and re-summed in rank order whenever a prefix lies within that scan's
+// rounding bound of p[h], so the decision is the rank-order one.  The first
+// rank whose running mass reaches p[h] fixes k*, and the key at rank k* - 1 is the threshold: block
 // j is kept when its key is not above it, which the lanes test on the
 // unsorted row (E consecutive indices each) to write the mask and, with a
 // wave scan of the counts, the ascending list.  Nothing depends on timing.
@@ -122,27 +124,65 @@ __global__ __launch_bounds__(kSelWaves * kWave) void select_kernel(
     }
   }
 
-  // k*: first rank whose fp64 running mass reaches p (ranks lane*E .. +E-1)
+  // k*: first rank whose running mass reaches p (ranks lane*E .. +E-1).
+  // The running mass is defined as the fp64 sum of the sorted fp32 scores
+  // taken one after another in rank order.  The fast path sums in-lane and
+  // scans across lanes, a different association; its prefixes differ from
+  // the rank-order ones by at most (2E + 6 + NB) fp64 roundings of the mass
+  // of absolute values, under 2^-40 of it for NB <= 4096.  When no prefix
+  // lies within twice that of p the two orders take the same decision;
+  // otherwise the row is summed again in rank order (one lane after another).
   const double p = static_cast<double>(top_p[h]);
   int kstar = NB;
   if (p < 1.0) {
-    double local = 0.0;
+    double local = 0.0, labs = 0.0;
 #pragma unroll
     for (int e = 0; e < E; ++e)
-      if (lane * E + e < NB) local += static_cast<double>(key_score(v[e]));
-    double total;
+      if (lane * E + e < NB) {
+        const double x = static_cast<double>(key_score(v[e]));
+        local += x;
+        labs += fabs(x);
+      }
+    double total, tabs;
     double run = wave_exclusive_scan<double>(local, total);
+    wave_exclusive_scan<double>(labs, tabs);
     int hit = 0x7fffffff;
+    double gap = INFINITY;  // distance of the nearest prefix to p
 #pragma unroll
     for (int e = 0; e < E; ++e) {
       const int r = lane * E + e;
-      if (r < NB && hit == 0x7fffffff) {
+      if (r < NB) {
         run += static_cast<double>(key_score(v[e]));
-        if (run >= p) hit = r;
+        gap = fmin(gap, fabs(run - p));
+        if (run >= p && hit == 0x7fffffff) hit = r;
       }
     }
 #pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) hit = min(hit, __shfl_xor(hit, o));
+    for (int o = 32; o >= 1; o >>= 1) {
+      hit = min(hit, __shfl_xor(hit, o));
+      gap = fmin(gap, __shfl_xor(gap, o));
+    }
+    if (gap <= ldexp(tabs, -39)) {
+      // near the threshold: the rank-order sum, lane by lane (rare)
+      double carry = 0.0;
+      hit = 0x7fffffff;
+      for (int L = 0; L < kWave && L * E < NB && hit == 0x7fffffff; ++L) {
+        double acc = carry;
+        int h2 = 0x7fffffff;
+        if (lane == L) {
+#pragma unroll
+          for (int e = 0; e < E; ++e) {
+            const int r = L * E + e;
+            if (r < NB) {
+              acc += static_cast<double>(key_score(v[e]));
+              if (acc >= p && h2 == 0x7fffffff) h2 = r;
+            }
+          }
+        }
+        carry = __shfl(acc, L);
+        hit = __shfl(h2, L);
+      }
+    }
     if (hit != 0x7fffffff) kstar = hit + 1;
   }
   if (max_blocks > 0 && kstar > max_blocks) kstar = max_blocks;

@@ -50,6 +50,8 @@ CASES = {
     "bf16_d64_b128": (2, (5, 16, 51), 64, 128, "bf16"),    # N=4080, NB=32, last block 112
     "bf16_d64_b64": (3, (4, 9, 37), 64, 64, "bf16"),       # N=1332, NB=21, last block 52
     "bf16_d128_b128_short": (3, (2, 13, 31), 128, 128, "bf16"),  # N=806, NB=7, last block 38 (< 64)
+    "bf16_d128_b128_even": (2, (5, 31, 81), 128, 128, "bf16"),  # N=12555, NB=99, last block 11 (4 chunks)
+    "bf16_d128_b64_big": (1, (2, 140, 160), 128, 64, "bf16"),   # N=44800, NB=700 (two-pass scorer)
     "fp32_tiny": (1, (4, 8, 8), 64, 64, "fp32"),           # the tiny workload itself
     "fp32_d128_b128": (2, (3, 10, 29), 128, 128, "fp32"),  # N=870, NB=7, last block 102
 }
@@ -355,3 +357,50 @@ def test_selection_large_rows(nb):
     for i in range(rows):
         sel, kstar, _, _ = O.select_row(s[0, i].astype(np.float64), 0.9)
         assert counts[0, i] == kstar and (idx[0, i, :kstar] == sel).all()
+
+
+def _rank_order_rows(nb, rng):
+    """Rows whose rank-order fp64 running mass crosses p far from where the
+    exact (or any reassociated) sum does: after 0.25 and 2^-25 - 2^-44 every
+    3 * 2^-56 rounds the rank-order sum up by a whole ulp (2^-54), so it
+    reaches p = 0.25 + 2^-25 after 1024 of them where the exact sum needs
+    1366.  The tiny values are scattered over the row; a second row puts four
+    2^-49 blocks ahead of them (rank-order count 902, exact 1201); in a third
+    the first three blocks sum to p exactly (inclusive boundary)."""
+    x, a = np.float32(3 * 2.0 ** -56), np.float32(2.0 ** -25 - 2.0 ** -44)
+    rows = []
+    r0 = np.zeros(nb, np.float32)
+    r0[0], r0[1], r0[2:1800] = 0.25, a, x
+    rows.append(r0)
+    r1 = r0.copy()
+    r1[1800:1804] = np.float32(2.0 ** -49)      # between a and x: taken before the tiny ones
+    rows.append(r1)
+    r2 = np.zeros(nb, np.float32)
+    r2[0], r2[1], r2[2] = 0.25, np.float32(2.0 ** -25 - 2.0 ** -44), np.float32(2.0 ** -44)
+    r2[3:600] = x                               # the prefix of three blocks is exactly p
+    rows.append(r2)
+    return [row[rng.permutation(nb)] for row in rows]
+
+
+def test_selection_follows_rank_order_sum_near_threshold():
+    """The selector's running mass is the fp64 sum in rank order (the
+    oracle's definition), also where a reassociated sum would cross p at
+    another rank: counts and lists equal the oracle's bit for bit."""
+    nb = 2048
+    say(f"[gpu] edge: rank-order running mass, NB={nb}")
+    rng = np.random.default_rng(77)
+    rows = _rank_order_rows(nb, rng)
+    s = np.zeros((1, nb, nb), np.float32)
+    for i, r in enumerate(rows):
+        s[0, i] = r
+    s[0, len(rows):len(rows) + 8] = rng.dirichlet(np.full(nb, 0.05), size=8)
+    q = torch.zeros((1, nb * 64, 64), dtype=torch.bfloat16)
+    p = R.make_problem(q, (1, 1, nb * 64), 64)
+    pth = np.float32(0.25 + 2.0 ** -25)
+    _, counts, idx, _ = R.select_topp(dev(torch.from_numpy(s)), dev(torch.tensor([pth])), p)
+    counts, idx = host(counts), host(idx)
+    for i in range(len(rows) + 8):
+        sel, kstar, _, csum = O.select_row(s[0, i].astype(np.float64), float(pth))
+        assert counts[0, i] == kstar and (idx[0, i, :kstar] == sel).all(), (i, int(counts[0, i]), kstar)
+    # the constructed rows do need the rank order: an exact sum would keep more blocks
+    assert O.select_row(s[0, 0].astype(np.float64), float(pth))[1] == 1026
