@@ -58,6 +58,12 @@ def parse():
     ap.add_argument("--clusters", action="store_true",
                     help="report PARK's query-aware key clusters against contiguous blocks instead")
     ap.add_argument("--kmeans-iters", type=int, default=5, help="Lloyd iterations for --clusters")
+    ap.add_argument("--no-extra", dest="extra", action="store_false",
+                    help="time only the named workload (no HunyuanVideo / 480p sub-records, no reuse trajectory)")
+    ap.add_argument("--traj-steps-bench", type=int, default=50,
+                    help="length of the reuse trajectory reported beside the 720p step")
+    ap.add_argument("--attn-traffic-probe", action="store_true",
+                    help="only run the attention kernel on 2048 one-block heads (counter calibration)")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of MIB MiB (HBM counter calibration)")
     return ap.parse_args()
@@ -68,16 +74,20 @@ def source_hash(path):
 
 
 def profiled_traffic(workload):
-    """HBM bytes per attention launch from the committed PMC summary, if it
-    covers this workload and the current attention source."""
+    """Fabric bytes per attention launch from the committed counter summary,
+    if it covers this workload and the current attention source."""
     if workload != WORKLOAD or not os.path.exists(ATTN_PROFILE):
         return None
     text = open(ATTN_PROFILE).read()
     m_hash = re.search(r"attn\.hip sha256\[:16\]: (\w+)", text)
-    m_bytes = re.search(r"hbm_bytes_per_launch: ([0-9.eE+]+)", text)
-    if not m_hash or not m_bytes or m_hash.group(1) != source_hash(ATTN_SOURCE):
+    m_bytes = re.search(r"fabric_bytes_per_launch: ([0-9.eE+]+)", text)
+    m_raw = re.search(r"raw_kib_per_launch: fetch ([0-9]+) write ([0-9]+)", text)
+    m_scale = re.search(r"scale: fetch ([0-9.]+) write ([0-9.]+)", text)
+    if not (m_hash and m_bytes and m_raw and m_scale) or m_hash.group(1) != source_hash(ATTN_SOURCE):
         return None
-    return float(m_bytes.group(1))
+    return {"scaled": float(m_bytes.group(1)),
+            "raw_kib": {"fetch": int(m_raw.group(1)), "write": int(m_raw.group(2))},
+            "scale": {"fetch": float(m_scale.group(1)), "write": float(m_scale.group(2))}}
 
 
 def executed_flops(counts, idx, wl):
@@ -201,6 +211,32 @@ def copy_reference(dev, mib=1024, reps=10, trials=3):
         rates.append(2.0 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9)
     del a, b
     return float(sorted(rates)[len(rates) // 2])
+
+
+def attn_traffic_probe():
+    """Counter calibration with the attention kernel's own loads: 2048 heads
+    of one 128-token block each (head_dim 128, bf16, every list = the one
+    block), so each workgroup reads its Q, K and V^T tiles exactly once and
+    writes its output and lse once.  Read bytes per launch: 2048 x 3 x 32 KiB
+    = 192 MiB (the V^T relayout is a kernel of its own); written: 2048 x
+    (32 KiB + 512 B)."""
+    import torch
+    import block_sparse_attention_scoring_amd as R
+    dev = "cuda:0"
+    H, N, D = 2048, 128, 128
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    q, k, v = (torch.randn(H, N, D, device=dev, generator=g).to(torch.bfloat16) for _ in range(3))
+    p = R.make_problem(q, (1, 1, N), 128)
+    counts = torch.ones(H, 1, dtype=torch.int32, device=dev)
+    idx = torch.zeros(H, 1, 1, dtype=torch.int32, device=dev)
+    out, lse = R.block_sparse_attn(q, k, v, counts, idx, p)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        R.block_sparse_attn(q, k, v, counts, idx, p, out=out, lse=lse)
+    torch.cuda.synchronize()
+    print(json.dumps({"attn_traffic_probe": {"read_bytes": 3 * H * N * D * 2,
+                                             "write_bytes": H * N * D * 2 + H * N * 4, "launches": 4}}))
 
 
 def copy_probe(mib):
@@ -512,6 +548,9 @@ def main():
     if args.copy_probe:
         copy_probe(args.copy_probe)
         return
+    if args.attn_traffic_probe:
+        attn_traffic_probe()
+        return
     if args.retrieval:
         retrieval(args)
         return
@@ -525,14 +564,121 @@ def main():
     import numpy as np
     import torch
     import workloads as W
-    import block_sparse_attention_scoring_amd as R
 
     wl = W.CONFIGS[args.workload]
-    t_gen = time.perf_counter()
-    inp = W.make_inputs(wl)
-    t_gen = time.perf_counter() - t_gen
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    t_gen = time.perf_counter()
+    # the 720p reuse trajectory starts from the 720p workload's own inputs
+    # (same seeds), so one generation with the fp32 masters serves both
+    traj_wl = W.CONFIGS["reuse_720p"]
+    with_traj = args.extra and wl.name == "wan14b_720p"
+    inp = W.make_inputs(traj_wl if with_traj else wl, keep_masters=with_traj)
+    t_gen = time.perf_counter() - t_gen
+    print(json.dumps({"progress": f"{wl.name}: inputs generated in {t_gen:.1f} s"}), file=sys.stderr, flush=True)
+    m = measure(wl, inp, dev, args.steps, args.warmup)
+    flops, per, ms_step = m["flops"], m["per"], m["ms_step"]
+    dense_flops = 4.0 * wl.tokens * wl.tokens * wl.head_dim * wl.heads
+    attn_tflops = flops / (per["attn"] * 1e-3) / 1e12
+    res = {
+        "metric": "ms per block-sparse attention call + effective TFLOP/s at 720p DiT shape",
+        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "fp32",
+        "data": f"synthetic (seeded smooth 3-D field + noise, {wl.name} latent shape; no weights)",
+        "config": {
+            "workload": wl.name, "heads": wl.heads, "grid": list(wl.grid), "tokens": wl.tokens,
+            "head_dim": wl.head_dim, "block": wl.block,
+            # one value, or the per-head pattern (head h takes entry h mod its length)
+            "top_p": wl.top_p[0] if len(set(wl.top_p)) == 1 else list(wl.top_p),
+            "parallelism": "single GPU",
+        },
+        "attn_ms_per_call": round(per["attn"], 3),
+        "attn_effective_tflops": round(attn_tflops, 1),
+        "attn_dense_equivalent_tflops": round(dense_flops / (per["attn"] * 1e-3) / 1e12, 1),
+        **summary(wl, m),
+        "input_generation_s": round(t_gen, 1),
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(attn_tflops, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
+            "kernel": attn_kernel_name(wl),
+            # HIP events bracket the whole library call, which also runs the
+            # V^T relayout and list canonicalisation kernels (about 1%)
+            "timed": "rsa_block_sparse_attn call",
+            **traffic_fields(wl, m),
+        },
+    }
+    if not args.no_gemm_reference and wl.dtype == "bf16":
+        gemm = gemm_reference(dev)
+        res["roofline"]["vendor_gemm"] = {
+            "value": round(gemm, 1), "unit": "TFLOP/s", "attn_frac": round(attn_tflops / gemm, 4),
+            "what": "torch.matmul bf16 8192^3 (hipBLASLt), same GPU, after the timed steps",
+        }
+        copy = copy_reference(dev)
+        res["vendor_copy"] = {
+            "value": round(copy, 1), "unit": "GB/s",
+            "drift_over_copy": round(m["drift_bytes"] / (per["drift"] * 1e-3) / 1e9 / copy, 4),
+            "what": "torch copy of 1 GiB (bytes read + written), same GPU, after the timed steps",
+        }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(inp, wl, m["counts"], m["idx"], flops)
+    if args.extra:
+        # the other single-GPU workloads of the same family, in the same run
+        subs = {}
+        for name in ("hunyuan_720p", "wan13b_480p"):
+            if name == wl.name:
+                continue
+            w2 = W.CONFIGS[name]
+            i2 = W.make_inputs(w2)
+            m2 = measure(w2, i2, dev, max(3, args.steps // 2), max(1, args.warmup))
+            t2 = m2["flops"] / (m2["per"]["attn"] * 1e-3) / 1e12
+            subs[name] = {
+                "heads": w2.heads, "grid": list(w2.grid), "tokens": w2.tokens, "block": w2.block,
+                "top_p": w2.top_p[0] if len(set(w2.top_p)) == 1 else list(w2.top_p),
+                "steps": max(3, args.steps // 2),
+                "attn_ms_per_call": round(m2["per"]["attn"], 3),
+                "attn_effective_tflops": round(t2, 1),
+                "roofline_frac": round(t2 / PEAK_BF16_TFLOPS, 4),
+                "kernel": attn_kernel_name(w2),
+                "ms_per_step": round(m2["ms_step"], 3),
+                **summary(w2, m2),
+            }
+            del i2, m2
+            torch.cuda.empty_cache()
+            print(json.dumps({"progress": {name: subs[name]["attn_ms_per_call"]}}), file=sys.stderr, flush=True)
+        res["workloads"] = subs
+        if with_traj:
+            res["reuse_trajectory"] = trajectory(traj_wl, inp, dev, args.traj_steps_bench)
+    print(json.dumps(res), flush=True)
+
+
+def attn_kernel_name(wl):
+    """The attention kernel instantiation a workload launches (csrc/attn.hip):
+    128 query rows per workgroup, 32-key sub-tiles; 128-token blocks keep a
+    three-slot ring, 64-token blocks run in pairs with a four-slot ring."""
+    if wl.dtype != "bf16":
+        return f"attn_f32_kernel<{wl.head_dim},{wl.block}>"
+    nbuf = 4 if wl.block == 64 else 3
+    return f"attn_bf16_kernel<{wl.head_dim},128,32,{nbuf},false,{wl.block}>"
+
+
+def measure(wl, inp, dev, steps, warmup):
+    """Time the step (drift -> score -> select -> attention) on one workload:
+    per-call HIP-event times on the library's stream, averaged over `steps`."""
+    import numpy as np
+    import torch
+    import block_sparse_attention_scoring_amd as R
+
     q, k, v = (t.to(dev) for t in (inp.q, inp.k, inp.v))
     p = R.make_problem(q, wl.grid, wl.block)
     nb = wl.nblocks
@@ -570,91 +716,126 @@ def main():
             if events is not None:
                 events[j][1].record(stream)
 
-    for _ in range(args.warmup):
+    for _ in range(warmup):
         step()
     torch.cuda.synchronize()
     ev = [[[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in names]
-          for _ in range(args.steps)]
+          for _ in range(steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for s in range(args.steps):
+    for s in range(steps):
         step(ev[s])
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    per = {n: float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(args.steps)]))
+    per = {n: float(np.mean([ev[s][j][0].elapsed_time(ev[s][j][1]) for s in range(steps)]))
            for j, n in enumerate(names)}
-    ms_step = wall * 1e3 / args.steps
-
     c_h, i_h = counts.cpu().numpy(), idx.cpu().numpy()
-    flops = executed_flops(c_h, i_h, wl)
-    dense_flops = 4.0 * wl.tokens * wl.tokens * wl.head_dim * wl.heads
-    dens = density.cpu().numpy()
-    attn_tflops = flops / (per["attn"] * 1e-3) / 1e12
-    # scoring's algorithmic HBM bytes: q and k read once, scores written once
     esz = 2 if wl.dtype == "bf16" else 4
-    score_bytes = 2.0 * wl.heads * wl.tokens * wl.head_dim * esz + 4.0 * wl.heads * nb * nb
-    drift_bytes = 4.0 * wl.heads * wl.tokens * wl.head_dim * esz
+    return {
+        "per": per, "ms_step": wall * 1e3 / steps, "counts": c_h, "idx": i_h,
+        "flops": executed_flops(c_h, i_h, wl), "density": density.cpu().numpy(),
+        # scoring's algorithmic HBM bytes: q and k read once, scores written once
+        "score_bytes": 2.0 * wl.heads * wl.tokens * wl.head_dim * esz + 4.0 * wl.heads * nb * nb,
+        "drift_bytes": 4.0 * wl.heads * wl.tokens * wl.head_dim * esz,
+        # attention's algorithmic HBM bytes: q, k, v read once, out written once, lse written once
+        "attn_bytes": 4.0 * wl.heads * wl.tokens * wl.head_dim * esz + 4.0 * wl.heads * wl.tokens,
+    }
 
-    res = {
-        "metric": "ms per block-sparse attention call + effective TFLOP/s at 720p DiT shape",
-        "value": round(flops / (ms_step * 1e-3) / 1e12, 2),
-        "unit": "TFLOP/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_step, 3),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "bf16",
-        "data": "synthetic (seeded smooth 3-D field + noise, Wan2.1-14B 720p latent shape; no weights)",
-        "config": {
-            "workload": wl.name, "heads": wl.heads, "grid": list(wl.grid), "tokens": wl.tokens,
-            "head_dim": wl.head_dim, "block": wl.block,
-            # one value, or the per-head pattern (head h takes entry h mod its length)
-            "top_p": wl.top_p[0] if len(set(wl.top_p)) == 1 else list(wl.top_p),
-            "parallelism": "single GPU",
-        },
-        "attn_ms_per_call": round(per["attn"], 3),
-        "attn_effective_tflops": round(attn_tflops, 1),
-        "attn_dense_equivalent_tflops": round(dense_flops / (per["attn"] * 1e-3) / 1e12, 1),
+
+def summary(wl, m):
+    """Per-kernel times and the bandwidth/matrix figures of the non-attention calls."""
+    per, dens = m["per"], m["density"]
+    nbp = -(-wl.nblocks // 32) * 32
+    # the scorer's matrix work: two passes x two fp16 terms over NB padded to 32
+    score_flops = 2 * 2 * 2.0 * wl.tokens * nbp * wl.head_dim * wl.heads
+    return {
         "score_ms": round(per["score"], 3),
         "select_ms": round(per["select"], 3),
         "drift_ms": round(per["drift"], 3),
-        "score_hbm_gbs": round(score_bytes / (per["score"] * 1e-3) / 1e9, 1),
-        "score_hbm_frac": round(score_bytes / (per["score"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "drift_hbm_gbs": round(drift_bytes / (per["drift"] * 1e-3) / 1e9, 1),
+        "score_hbm_gbs": round(m["score_bytes"] / (per["score"] * 1e-3) / 1e9, 1),
+        "score_hbm_frac": round(m["score_bytes"] / (per["score"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+        "score_mfma_frac": round(score_flops / (per["score"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "drift_hbm_gbs": round(m["drift_bytes"] / (per["drift"] * 1e-3) / 1e9, 1),
+        "drift_hbm_frac": round(m["drift_bytes"] / (per["drift"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
         "density_mean": round(float(dens.mean()), 4),
         "density_min_max": [round(float(dens.min()), 4), round(float(dens.max()), 4)],
-        "executed_tflop_per_step": round(flops / 1e12, 3),
-        "input_generation_s": round(t_gen, 1),
-        "roofline": {
-            "bound": "mfma",
-            "achieved": round(attn_tflops, 1),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4),
-            "traffic": profiled_traffic(wl.name),
-            "kernel": "attn_bf16_kernel<128,128,32,3>",
-            # HIP events bracket the whole library call, which also runs the
-            # V^T relayout and list canonicalisation kernels (about 1%)
-            "timed": "rsa_block_sparse_attn call",
-        },
+        "executed_tflop_per_step": round(m["flops"] / 1e12, 3),
     }
-    if not args.no_gemm_reference and wl.dtype == "bf16":
-        gemm = gemm_reference(dev)
-        res["roofline"]["vendor_gemm"] = {
-            "value": round(gemm, 1), "unit": "TFLOP/s", "attn_frac": round(attn_tflops / gemm, 4),
-            "what": "torch.matmul bf16 8192^3 (hipBLASLt), same GPU, after the timed steps",
-        }
-        copy = copy_reference(dev)
-        res["vendor_copy"] = {
-            "value": round(copy, 1), "unit": "GB/s", "drift_over_copy": round(drift_bytes / (per["drift"] * 1e-3) / 1e9 / copy, 4),
-            "what": "torch copy of 1 GiB (bytes read + written), same GPU, after the timed steps",
-        }
-    if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(inp, wl, c_h, i_h, flops)
-    print(json.dumps(res), flush=True)
+
+
+def trajectory(wl, inp, dev, steps):
+    """The 720p reuse trajectory through MaskCache.step: q and k take the
+    generator's random walk, each head refreshes its mask when its drift
+    passes the threshold.  Per step: the whole cache.step on the library's
+    stream (HIP events), the heads refreshed and the mean density.  The next
+    step's inputs are generated on the host while the GPU runs."""
+    import numpy as np
+    import torch
+    import workloads as W
+    import block_sparse_attention_scoring_amd as R
+
+    stream = torch.cuda.current_stream(dev)
+    v = inp.v.to(dev)
+    p = R.make_problem(v, wl.grid, wl.block)
+    cache = R.MaskCache(p, torch.from_numpy(inp.top_p).to(dev), wl.drift_threshold)
+    out = torch.empty_like(v)
+    lse = torch.empty((wl.heads, wl.tokens), dtype=torch.float32, device=dev)
+    rows = []
+    q, k = inp.q.to(dev), inp.k.to(dev)
+    for s in range(steps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        cache.step(q, k, v, out=out, lse=lse)
+        e1.record(stream)
+        # the next step's inputs are generated on the host while the GPU runs
+        # this one (launching first keeps host work out of the timed launches)
+        if s + 1 < steps:
+            W.drift_step(inp, s + 1)
+        torch.cuda.synchronize()
+        fl = cache.refresh.cpu().numpy() if s > 0 else np.ones(wl.heads, np.uint8)
+        rows.append((s, float(e0.elapsed_time(e1)), fl.copy(), float(cache.density.mean().item())))
+        if s + 1 < steps:
+            q, k = inp.q.to(dev), inp.k.to(dev)
+        if s % 10 == 9 or s == steps - 1:
+            print(json.dumps({"progress": {"trajectory_step": s, "ms": round(rows[-1][1], 3),
+                                           "refreshed": int(fl.sum())}}), file=sys.stderr, flush=True)
+    ms = np.array([r[1] for r in rows])
+    nref = np.array([int(r[2].sum()) for r in rows])
+    counts = np.sum([r[2] for r in rows], axis=0)
+    reuse = ms[1:][nref[1:] == 0]
+    part = ms[1:][nref[1:] > 0]
+    return {
+        "workload": wl.name, "steps": steps, "drift_threshold": wl.drift_threshold,
+        "timed": "MaskCache.step (drift, gated scoring and selection, attention with the lists in force)",
+        "ms_step0_all_heads_refresh": round(float(ms[0]), 3),
+        "ms_reuse_step_mean": round(float(reuse.mean()), 3) if reuse.size else None,
+        "reuse_steps": int(reuse.size),
+        "ms_partial_refresh_step_mean": round(float(part.mean()), 3) if part.size else None,
+        "partial_refresh_steps": int(part.size),
+        "ms_per_step_mean": round(float(ms.mean()), 3),
+        "refreshed_heads_per_step": nref.tolist(),
+        "refresh_count_per_head": counts.astype(int).tolist(),
+        "density_per_step": [round(r[3], 4) for r in rows],
+        "ms_per_step": [round(float(x), 3) for x in ms],
+    }
+
+
+def traffic_fields(wl, m):
+    """roofline.traffic from the committed counter summary, when it was taken
+    on this workload and the current attention source: FETCH_SIZE and
+    WRITE_SIZE count bytes between the L2 caches and the memory fabric (the
+    256 MB Infinity Cache serves part of them), scaled by what the same
+    counters read for a kernel that streams a buffer of known size with the
+    attention kernel's own 16-byte direct-to-LDS loads."""
+    t = profiled_traffic(wl.name)
+    out = {"traffic": None, "algorithmic_bytes": round(m["attn_bytes"])}
+    if t is not None:
+        out["traffic"] = t["scaled"]
+        out["traffic_what"] = "L2<->fabric bytes per launch (FETCH_SIZE + WRITE_SIZE, scaled), not HBM bytes"
+        out["traffic_raw_kib"] = t["raw_kib"]
+        out["traffic_scale"] = t["scale"]
+        out["traffic_over_algorithmic"] = round(t["scaled"] / m["attn_bytes"], 1)
+    return out
 
 
 if __name__ == "__main__":
