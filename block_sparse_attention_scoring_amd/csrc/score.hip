@@ -315,23 +315,25 @@ __global__ __launch_bounds__(2 * B, NBUF == 3 ? 3 : 2) void score_kernel(
   auto logits = [&](int c, const _Float16* cur, auto kTr) __attribute__((always_inline)) {
     const char* th = reinterpret_cast<const char*>(cur);
     const char* tl = reinterpret_cast<const char*>(cur + kTile);
-    f32x16 acc_hi = f32x16{}, acc_lo = f32x16{};
+    // hi and lo terms in one accumulation chain (several waves per SIMD
+    // interleave their chains; two chains would cost 16 adds per chunk)
+    f32x16 acc = f32x16{};
 #pragma unroll
     for (int s = 0; s < kKS; ++s) {
       const int o = col * (2 * D) + (((2 * s + hl) ^ swz<kCpr>(col)) * 16);
       const f16x8 ah = *reinterpret_cast<const f16x8*>(th + o);
       const f16x8 al = *reinterpret_cast<const f16x8*>(tl + o);
       if constexpr (decltype(kTr)::value) {
-        acc_hi = mfma32(ah, qh[s], acc_hi);
-        acc_lo = mfma32(al, qh[s], acc_lo);
-        if constexpr (kSplitQ) acc_lo = mfma32(ah, ql[s], acc_lo);
+        acc = mfma32(ah, qh[s], acc);
+        acc = mfma32(al, qh[s], acc);
+        if constexpr (kSplitQ) acc = mfma32(ah, ql[s], acc);
       } else {
-        acc_hi = mfma32(qh[s], ah, acc_hi);
-        acc_lo = mfma32(qh[s], al, acc_lo);
-        if constexpr (kSplitQ) acc_lo = mfma32(ql[s], ah, acc_lo);
+        acc = mfma32(qh[s], ah, acc);
+        acc = mfma32(qh[s], al, acc);
+        if constexpr (kSplitQ) acc = mfma32(ql[s], ah, acc);
       }
     }
-    return acc_hi + acc_lo;
+    return acc;
   };
 
   float mraw = -INFINITY, z = 0.f;  // pass 1, this half's key blocks
