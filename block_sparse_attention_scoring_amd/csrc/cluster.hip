@@ -13,8 +13,9 @@
 //           products of exact bf16 values, fp32 sums), then the chunks added
 //           in a fixed order in fp64 and divided by N.
 //   k-means iteration (Lloyd):
-//     wprep   W_j = 2 G c_j and b_j = c_j^T G c_j for every centroid; W split
-//             into two bf16 terms (16 significant bits) for the matrix cores;
+//     wprep   W_j = 2 G c_j and b_j = c_j^T G c_j for every centroid; W_j
+//             times its own power of two split into two fp16 terms (22
+//             significant bits) for the matrix cores;
 //     assign  the nearest centroid maximises 2 k.G c_j - c_j^T G c_j: one
 //             workgroup per 128 keys, the keys in registers, centroid chunks of
 //             32 streamed through LDS, a running maximum per key (ties: the
@@ -118,16 +119,18 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restric
 }
 
 // ---------------------------------------------------------------- wprep
-// For 32 centroids per workgroup: W_j = 2 G c_j (fp32, e ascending), split
-// into bf16 hi + lo, and b_j = c_j . (G c_j).  Rows past NB get zero W and
-// b = +inf, so they never win the assignment.
+// For 32 centroids per workgroup: W_j = 2 G c_j (fp32) and b_j = c_j . (G c_j);
+// W_j times its own power of two t_j (max |W_j t_j| in [2^13, 2^14)) split
+// into fp16 hi + lo, 22 significant bits, and 1 / t_j.  Rows past NB get zero
+// W and b = +inf, so they never win the assignment.
 template <int D>
 __global__ __launch_bounds__(256) void wprep_kernel(const float* __restrict__ gram, const float* __restrict__ cent,
-                                                    uint16_t* __restrict__ whi, uint16_t* __restrict__ wlo,
-                                                    float* __restrict__ w32, float* __restrict__ bvec, int NB,
-                                                    int NBp) {
+                                                    _Float16* __restrict__ whi, _Float16* __restrict__ wlo,
+                                                    float* __restrict__ w32, float* __restrict__ bvec,
+                                                    float* __restrict__ winv, int NB, int NBp) {
   __shared__ float cs[32][D];
   __shared__ float ws[32][D + 1];
+  __shared__ float tsc[32];
   const int j0 = blockIdx.x * 32, h = blockIdx.y, tid = threadIdx.x;
   const float* g = gram + static_cast<size_t>(h) * D * D;  // read by rows: neighbouring threads, neighbouring d
   for (int e = tid; e < 32 * D; e += 256) {
@@ -141,58 +144,94 @@ __global__ __launch_bounds__(256) void wprep_kernel(const float* __restrict__ gr
 #pragma unroll 8
     for (int x = 0; x < D; ++x) acc = fmaf(g[x * D + d], cs[j][x], acc);  // G symmetric: G[d][x] = G[x][d]
     ws[j][d] = acc;
-    const float w2 = 2.f * acc;
-    const __bf16 hi = static_cast<__bf16>(w2);
-    const __bf16 lo = static_cast<__bf16>(w2 - static_cast<float>(hi));
-    const size_t o = (static_cast<size_t>(h) * NBp + j0 + j) * D + d;
-    whi[o] = __builtin_bit_cast(uint16_t, hi);
-    wlo[o] = __builtin_bit_cast(uint16_t, lo);
-    w32[o] = w2;
+    w32[(static_cast<size_t>(h) * NBp + j0 + j) * D + d] = 2.f * acc;
   }
   __syncthreads();
   if (tid < 32) {
-    float b = 0.f;
-    for (int d = 0; d < D; ++d) b = fmaf(cs[tid][d], ws[tid][d], b);
-    bvec[static_cast<size_t>(h) * NBp + j0 + tid] = j0 + tid < NB ? b : INFINITY;
+    float b = 0.f, m = 0.f;
+    for (int d = 0; d < D; ++d) {
+      b = fmaf(cs[tid][d], ws[tid][d], b);
+      m = fmaxf(m, fabsf(2.f * ws[tid][d]));
+    }
+    const int sh = (m > 0.f && m < INFINITY) ? 13 - ilog2f(m) : 0;
+    const int shc = sh < -126 ? -126 : (sh > 126 ? 126 : sh);
+    tsc[tid] = pow2i(shc);
+    const size_t o = static_cast<size_t>(h) * NBp + j0 + tid;
+    bvec[o] = j0 + tid < NB ? b : INFINITY;
+    winv[o] = pow2i(-shc);
+  }
+  __syncthreads();
+  for (int e = tid; e < 32 * D; e += 256) {
+    const int j = e / D, d = e % D;
+    const float x = 2.f * ws[j][d] * tsc[j];
+    const _Float16 hi = static_cast<_Float16>(x);
+    const size_t o = (static_cast<size_t>(h) * NBp + j0 + j) * D + d;
+    whi[o] = hi;
+    wlo[o] = static_cast<_Float16>(x - static_cast<float>(hi));
   }
 }
 
 // ---------------------------------------------------------------- assign
 // One workgroup per 128 keys (4 waves of 32).  Each lane holds its key's
-// dims 16s + 8hl..+7 in registers (bf16, exact).  Centroid chunks of 32
-// (W hi and lo tiles, swizzled) go through LDS; S^T = W K^T puts the 16
-// clusters 32c + acc_row(r, hl) of this lane's key in its registers, so the
-// running maximum of 2 k.G c_j - b_j stays in-lane; the halves merge last.
+// dims 16s + 8hl..+7 in registers as fp16, scaled by the key's own power of
+// two s_k (exact for bf16 keys).  Centroid chunks of 32 (W_j t_j hi and lo
+// tiles, swizzled) go through LDS; S^T = W K^T puts the 16 clusters
+// 32c + acc_row(r, hl) of this lane's key in its registers, both terms in one
+// accumulation chain, so 2 k.G c_j = acc / (t_j s_k) to about fp32 accuracy
+// (the unscaling is exact) and the running maximum of 2 k.G c_j - b_j stays
+// in-lane; the halves merge last.
 template <int D>
 __global__ __launch_bounds__(256) void assign_bf16_kernel(const uint16_t* __restrict__ k,
-                                                          const uint16_t* __restrict__ whi,
-                                                          const uint16_t* __restrict__ wlo,
+                                                          const _Float16* __restrict__ whi,
+                                                          const _Float16* __restrict__ wlo,
                                                           const float* __restrict__ bvec,
+                                                          const float* __restrict__ winv,
                                                           int* __restrict__ labels, int N, int NBp) {
   constexpr int kKS = D / 16, kCpr = D / 8;
-  __shared__ __attribute__((aligned(16))) uint16_t th[32 * D];
-  __shared__ __attribute__((aligned(16))) uint16_t tl[32 * D];
-  __shared__ float bs[32];
+  __shared__ __attribute__((aligned(16))) _Float16 th[32 * D];
+  __shared__ __attribute__((aligned(16))) _Float16 tl[32 * D];
+  __shared__ float bs[32], ts[32];
   const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, col = lane & 31;
   const int t = blockIdx.x * kAssignRows + wave * 32 + col;
-  bf16x8 kf[kKS];
+  f16x8 kf[kKS];
+  float kinv;
   {
     const bool ok = t < N;
     const u32x4* src = reinterpret_cast<const u32x4*>(k + (static_cast<size_t>(h) * N + (ok ? t : 0)) * D);
+    float x[kKS][8];
+    float a = 0.f;
 #pragma unroll
-    for (int s = 0; s < kKS; ++s) kf[s] = __builtin_bit_cast(bf16x8, ok ? src[2 * s + hl] : u32x4{0, 0, 0, 0});
+    for (int s = 0; s < kKS; ++s) {
+      const u32x4 raw = ok ? src[2 * s + hl] : u32x4{0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        x[s][2 * e] = __uint_as_float(raw[e] << 16);
+        x[s][2 * e + 1] = __uint_as_float(raw[e] & 0xffff0000u);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) a = fmaxf(a, fabsf(x[s][e]));
+    }
+    a = fmaxf(a, __shfl_xor(a, 32));  // the other half of the key
+    const int sh0 = (a > 0.f && a < INFINITY) ? 13 - ilog2f(a) : 0;
+    const int sh = sh0 < -126 ? -126 : (sh0 > 126 ? 126 : sh0);
+    const float sf = pow2i(sh);
+#pragma unroll
+    for (int s = 0; s < kKS; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) kf[s][e] = static_cast<_Float16>(x[s][e] * sf);
+    kinv = pow2i(-sh);
   }
-  const uint16_t* wh = whi + static_cast<size_t>(h) * NBp * D;
-  const uint16_t* wl = wlo + static_cast<size_t>(h) * NBp * D;
+  const _Float16* wh = whi + static_cast<size_t>(h) * NBp * D;
+  const _Float16* wl = wlo + static_cast<size_t>(h) * NBp * D;
   float best = -INFINITY;
   int bj = 0;
   // the next chunk is loaded into registers while this one is multiplied
   constexpr int kPerThread = 32 * kCpr / 256;
   static_assert(32 * kCpr % 256 == 0, "chunk not divisible");
   u32x4 nh[kPerThread], nl[kPerThread];
-  float nb = 0.f;
+  float nb = 0.f, nt = 0.f;
   auto fetch = [&](int c) {
 #pragma unroll
     for (int i = 0; i < kPerThread; ++i) {
@@ -201,7 +240,10 @@ __global__ __launch_bounds__(256) void assign_bf16_kernel(const uint16_t* __rest
       nh[i] = *reinterpret_cast<const u32x4*>(wh + g);
       nl[i] = *reinterpret_cast<const u32x4*>(wl + g);
     }
-    if (tid < 32) nb = bvec[static_cast<size_t>(h) * NBp + 32 * c + tid];
+    if (tid < 32) {
+      nb = bvec[static_cast<size_t>(h) * NBp + 32 * c + tid];
+      nt = winv[static_cast<size_t>(h) * NBp + 32 * c + tid];
+    }
   };
   fetch(0);
   for (int c = 0; c < NBp / 32; ++c) {
@@ -213,20 +255,23 @@ __global__ __launch_bounds__(256) void assign_bf16_kernel(const uint16_t* __rest
       *reinterpret_cast<u32x4*>(&th[dst]) = nh[i];
       *reinterpret_cast<u32x4*>(&tl[dst]) = nl[i];
     }
-    if (tid < 32) bs[tid] = nb;
+    if (tid < 32) {
+      bs[tid] = nb;
+      ts[tid] = nt;
+    }
     __syncthreads();
     if (c + 1 < NBp / 32) fetch(c + 1);
-    f32x16 ah = f32x16{}, al = f32x16{};
+    f32x16 acc = f32x16{};
 #pragma unroll
     for (int s = 0; s < kKS; ++s) {
       const int o = col * D + ((2 * s + hl) ^ swz<kCpr>(col)) * 8;
-      ah = mfma32(*reinterpret_cast<const bf16x8*>(&th[o]), kf[s], ah);
-      al = mfma32(*reinterpret_cast<const bf16x8*>(&tl[o]), kf[s], al);
+      acc = mfma32(*reinterpret_cast<const f16x8*>(&th[o]), kf[s], acc);
+      acc = mfma32(*reinterpret_cast<const f16x8*>(&tl[o]), kf[s], acc);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int jr = acc_row(r, hl);
-      const float v = (ah[r] + al[r]) - bs[jr];
+      const float v = acc[r] * ts[jr] * kinv - bs[jr];   // the two products by powers of two are exact
       if (v > best) {  // rows ascend with r: the first maximum is the lowest index
         best = v;
         bj = 32 * c + jr;
@@ -431,8 +476,8 @@ __global__ __launch_bounds__(D) void seg_combine_kernel(const double* __restrict
 }
 
 struct KmeansWs {
-  uint16_t *whi, *wlo;
-  float *w32, *bvec, *bmax;
+  _Float16 *whi, *wlo;
+  float *w32, *bvec, *bmax, *winv;
   int *hist, *rank, *offs;
   double* part;
   size_t total;
@@ -448,13 +493,13 @@ KmeansWs kmeans_ws_layout(const Problem& p, void* base) {
   const size_t sizes[] = {al256(2 * H * NBp * D), al256(2 * H * NBp * D), al256(4 * H * NBp * D),
                           al256(4 * H * NBp), al256(4 * H * p.nb), al256(4 * H * nch * p.nb),
                           al256(4 * H * static_cast<size_t>(p.tokens)), al256(4 * H * p.nb),
-                          al256(8 * H * nseg * 2 * D)};
+                          al256(8 * H * nseg * 2 * D), al256(4 * H * NBp)};
   KmeansWs w{};
   char* b = static_cast<char*>(base);
   size_t off = 0;
   void** ptrs[] = {(void**)&w.whi, (void**)&w.wlo, (void**)&w.w32, (void**)&w.bvec, (void**)&w.bmax,
-                   (void**)&w.hist, (void**)&w.rank, (void**)&w.offs, (void**)&w.part};
-  for (int i = 0; i < 9; ++i) {
+                   (void**)&w.hist, (void**)&w.rank, (void**)&w.offs, (void**)&w.part, (void**)&w.winv};
+  for (int i = 0; i < 10; ++i) {
     if (b != nullptr) *ptrs[i] = b + off;
     off += sizes[i];
   }
@@ -478,11 +523,11 @@ hipError_t launch_kmeans_t(const Problem& p, const void* k, const float* gram, i
   }
   for (int it = 0; it < iters; ++it) {
     hipLaunchKernelGGL((wprep_kernel<D>), dim3(NBp / 32, H), dim3(256), 0, stream, gram, cent, w.whi, w.wlo,
-                       w.w32, w.bvec, NB, NBp);
+                       w.w32, w.bvec, w.winv, NB, NBp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (p.dtype == 0)
       hipLaunchKernelGGL((assign_bf16_kernel<D>), dim3((N + kAssignRows - 1) / kAssignRows, H), dim3(256), 0,
-                         stream, static_cast<const uint16_t*>(k), w.whi, w.wlo, w.bvec, labels, N, NBp);
+                         stream, static_cast<const uint16_t*>(k), w.whi, w.wlo, w.bvec, w.winv, labels, N, NBp);
     else
       hipLaunchKernelGGL((assign_f32_kernel<D>), dim3((N + 255) / 256, H), dim3(256), 0, stream,
                          static_cast<const float*>(k), w.w32, w.bvec, labels, N, NB, NBp);

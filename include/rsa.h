@@ -374,8 +374,10 @@ rsa_status rsa_query_gram(const rsa_problem* p, const void* q, float* gram, void
  *   order     [heads, tokens] int32: the keys sorted by (cluster, token), so
  *             cluster j is order[h, off_j .. off_j + sizes[h, j]) with off_j
  *             the sum of the sizes before j.
- * The assignment runs on the matrix cores with 2 gram c_j split into two bf16
- * terms (16 significant bits; fp64 products for fp32 keys); the sort is a
+ * The assignment runs on the matrix cores with 2 gram c_j times a power of two
+ * split into two fp16 terms (22 significant bits) and each key as fp16 times
+ * its own power of two (exact for bf16), so 2 k.gram c_j carries about fp32
+ * accuracy (fp64 products for fp32 keys); the sort is a
  * stable counting sort and the means are fp64 sums rounded once, so results
  * are deterministic.  ws / ws_bytes: at least rsa_workspace_bytes(p,
  * RSA_OP_KMEANS) bytes, 256-byte aligned.

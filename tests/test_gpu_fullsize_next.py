@@ -16,7 +16,7 @@ import torch
 import oracle as O
 import workloads as W
 import block_sparse_attention_scoring_amd as R
-from parity import rel_l2
+from parity import classify_row, rel_l2
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda:0"
@@ -121,6 +121,7 @@ def test_clusters_full_size():
     o_h, l_h, S_h = host(out.float()), host(lse), host(S)
     c, ix = host(counts), host(idx)
     near = 0
+    kinds = {"equal": 0, "tie": 0, "fail": 0}
     for h in heads:
         q64, k64, v64 = W.to_f64(inp.q[h]), W.to_f64(inp.k[h]), W.to_f64(inp.v[h])
         err = np.abs(g[h] - O.query_gram(q64)).max() / np.abs(g[h]).max()
@@ -132,16 +133,20 @@ def test_clusters_full_size():
             kt = k64[toks][diff]
             cs = c0[h][lab[h][toks][diff]]
             gap = dist[diff, lab[h][toks][diff]] - dist[diff, want[diff]]
-            assert (gap <= 1e-4 * (((kt @ g[h]) * kt).sum(1) + ((cs @ g[h]) * cs).sum(1))).all()
+            assert (gap <= 1e-6 * (((kt @ g[h]) * kt).sum(1) + ((cs @ g[h]) * cs).sum(1))).all()
             near += diff.size
         for j in rng.choice(np.flatnonzero(sz[h] > 0), 8, replace=False):
             np.testing.assert_allclose(cg[h, j], k64[lab[h] == j].mean(0), rtol=2 ** -23, atol=1e-30)
         s_or = O.cluster_scores(q64, cg[h], sz[h], wl.block, scale, query_blocks=rows)
         ds = float(np.abs(S_h[h, rows] - s_or).max())
         assert ds <= 1e-6, ds
+        for r, i in enumerate(rows):      # the cluster selection of each sampled row
+            kind, _ = classify_row(s_or[r], float(inp.top_p[h]), ix[h, i, :c[h, i]])
+            kinds[kind] += 1
+            assert kind != "fail", (h, i)
         sel = {i: ix[h, i, :c[h, i]] for i in rows}
         o_or, l_or = O.cluster_attention(q64, k64, v64, wl.block, lab[h], sel, scale, query_blocks=rows)
         check(f"720p cluster attention h={h} |dS| {ds:.1e}", o_h[h][tr], l_h[h][tr], o_or, l_or)
     say(f"[gpu] 720p clusters: density mean {float(dens.mean()):.4f}; near-tie labels among "
-        f"{256 * len(heads)} sampled keys: {near}")
+        f"{256 * len(heads)} sampled keys: {near}; cluster selection rows {kinds}")
     assert near <= 3
