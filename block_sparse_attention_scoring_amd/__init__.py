@@ -14,7 +14,7 @@ and run the clustered path.
 """
 from .binding import (Problem, RsaError, RsaLibraryMissing, attn_merge, attn_omitted,
                       block_sparse_attn, block_sparse_attn_corrected, cluster_attn, declared_functions, kmeans, query_gram, score_clusters,
-                      dense_block_mass, lib, make_problem, mask_drift, score_blocks,
+                      dense_block_mass, lib, make_problem, mask_drift, score_blocks, score_blocks_noalloc,
                       score_blocks_pooled, select_topp, workspace_bytes, OP_ATTN, OP_DRIFT,
                       OP_CLUSTER_ATTN, OP_GRAM, OP_KMEANS, OP_POOLED, OP_SCORE, OP_SELECT, RSA_BF16, RSA_FP32, LIB_PATH)
 from .cache import MaskCache
@@ -24,7 +24,8 @@ __all__ = [
     "block_sparse_attn_corrected",
     "cluster_attn", "declared_functions", "kmeans", "query_gram", "score_clusters", "OP_CLUSTER_ATTN",
     "OP_GRAM", "OP_KMEANS",
-    "dense_block_mass", "lib", "make_problem", "mask_drift", "score_blocks", "score_blocks_pooled",
+    "dense_block_mass", "lib", "make_problem", "mask_drift", "score_blocks", "score_blocks_noalloc",
+    "score_blocks_pooled",
     "select_topp", "workspace_bytes", "MaskCache", "OP_ATTN", "OP_DRIFT", "OP_POOLED", "OP_SCORE",
     "OP_SELECT", "RSA_BF16", "RSA_FP32", "LIB_PATH",
 ]

@@ -80,6 +80,7 @@ def _declare(lib):
         "rsa_kmeans": (i32, [pp, _P, _P, i32, i32, _P, _P, _P, _P, _P, sz, _P]),
         "rsa_score_clusters": (i32, [pp, _P, _P, _P, _P, _P, sz, _P]),
         "rsa_cluster_attn": (i32, [pp, _P, _P, _P, _P, _P, _P, _P, _P, _P, _P, sz, _P]),
+        "rsa_score_blocks_noalloc": (i32, [pp, _P, _P, _P, _P, _P]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -207,6 +208,21 @@ def score_blocks(q, k, p: Problem, head_active=None, out=None, workspace=None):
     ws, wsb = _workspace(p, OP_SCORE, q.device, workspace)
     _check(lib().rsa_score_blocks(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(head_active), _ptr(out),
                                   _ptr(ws), wsb, _stream(q)), "rsa_score_blocks")
+    return out
+
+
+def score_blocks_noalloc(q, k, p: Problem, head_active=None, out=None):
+    """PARK block scores with the library's static workspace (rsa_score_blocks_noalloc):
+    no device allocation by the library; ``out`` may be given to allocate nothing at all."""
+    _need_qkv(p, q=q, k=k)
+    _need(head_active, "head_active", torch.uint8, (p.heads,), optional=True)
+    _need(out, "out", torch.float32, (p.heads, p.nblocks, p.nblocks), optional=True)
+    _gpu(q=q, k=k, head_active=head_active, out=out)
+    nb = p.nblocks
+    if out is None:
+        out = torch.empty((p.heads, nb, nb), dtype=torch.float32, device=q.device)
+    _check(lib().rsa_score_blocks_noalloc(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(head_active), _ptr(out),
+                                          _stream(q)), "rsa_score_blocks_noalloc")
     return out
 
 

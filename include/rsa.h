@@ -435,6 +435,26 @@ rsa_status rsa_cluster_attn(const rsa_problem* p, const void* q, const void* k, 
                             const int32_t* order, const int32_t* counts, const int32_t* block_idx, void* out,
                             float* lse, void* ws, size_t ws_bytes, hipStream_t stream);
 
+/*
+ * rsa_score_blocks without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same inputs, output, results (bit for
+ * bit) and errors as rsa_score_blocks; the workspace is a static device array
+ * of RSA_NOALLOC_SCRATCH_BYTES that every GPU the library runs on holds until
+ * the process ends.  The call allocates nothing: its first call on a device
+ * looks up that device's copy of the array (hipGetSymbolAddress) and keeps the
+ * address.
+ * Errors: RSA_ERR_WORKSPACE when rsa_workspace_bytes(p, RSA_OP_SCORE) exceeds
+ * RSA_NOALLOC_SCRATCH_BYTES (64 MiB: e.g. 40 heads x 591 blocks of 128 need
+ * 25 MB), RSA_ERR_HIP when the array's address cannot be obtained; otherwise
+ * as rsa_score_blocks.
+ * All calls on one device share the array: calls that overlap in time on the
+ * same device (other streams, other host threads) race and must not be made.
+ */
+#define RSA_NOALLOC_SCRATCH_BYTES (64u << 20)
+rsa_status rsa_score_blocks_noalloc(const rsa_problem* p, const void* q, const void* k,
+                                    const uint8_t* head_active, float* scores, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -44,7 +44,7 @@ def test_exports_every_declared_symbol(lib):
                           "rsa_select_topp", "rsa_mask_drift", "rsa_block_sparse_attn",
                           "rsa_dense_block_mass", "rsa_score_blocks_pooled", "rsa_attn_omitted",
                           "rsa_attn_merge", "rsa_block_sparse_attn_corrected", "rsa_query_gram", "rsa_kmeans",
-                          "rsa_score_clusters", "rsa_cluster_attn"}
+                          "rsa_score_clusters", "rsa_cluster_attn", "rsa_score_blocks_noalloc"}
     for n in names:
         assert hasattr(lib, n), n
 
