@@ -672,30 +672,35 @@ __global__ __launch_bounds__(2 * B, NBUF == 3 ? 3 : 2) void attn_bf16_kernel(
   }
 }
 
-// fp32 inputs: plain fp32 arithmetic, one thread per query row, K and V
-// staged in LDS 32 keys at a time and read as broadcasts, over the canonical
-// list.  Same online softmax (exact rescaling at every chunk).
+// fp32 inputs: plain fp32 arithmetic over the canonical list, K and V staged
+// in LDS 32 keys at a time and read as broadcasts.  Each query row has two
+// lanes, l and l ^ 32 of a wave, each holding half of head_dim (query and
+// output in registers, loops fully unrolled, so nothing goes to scratch); a
+// score is the two halves' partial dot products added across the lane pair.
+// Same online softmax (exact rescaling at every 8 keys).
 // kTable: as in attn_bf16_kernel; k and v are the padded cluster layout,
 // row-major, Nk rows per head.
 template <int D, int B, bool kTable = false>
-__global__ __launch_bounds__(B) void attn_f32_kernel(
+__global__ __launch_bounds__(2 * B) void attn_f32_kernel(
     const float* __restrict__ q, const float* __restrict__ k, const float* __restrict__ v,
     const int* __restrict__ ccount, const int* __restrict__ clist,
     const uint8_t* __restrict__ head_active, const float* part, const float* part_lse, float* out, float* lse,
     int N, int NB, float scale_log2, int Nk, int lstride) {
   constexpr int kChunk = 32;
+  constexpr int DH = D / 2;  // dims per lane
   __shared__ float Ks[kChunk * D];
   __shared__ float Vs[kChunk * D];
   const int tile = xcd_remap(blockIdx.x, gridDim.x);
   const int h = tile / NB, I = tile - h * NB;
   if (head_active != nullptr && head_active[h] == 0) return;
-  const int tid = threadIdx.x;
-  const int qrow = I * B + tid;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int half = lane >> 5, d0 = half * DH;
+  const int qrow = I * B + (tid >> 6) * 32 + (lane & 31);
   const size_t head_off = static_cast<size_t>(h) * N * D;
-  float qv[D], o[D];
+  float qv[DH], o[DH];
 #pragma unroll
-  for (int d = 0; d < D; ++d) {
-    qv[d] = qrow < N ? q[head_off + static_cast<size_t>(qrow) * D + d] * scale_log2 : 0.f;
+  for (int d = 0; d < DH; ++d) {
+    qv[d] = qrow < N ? q[head_off + static_cast<size_t>(qrow) * D + d0 + d] * scale_log2 : 0.f;
     o[d] = 0.f;
   }
   float m = -INFINITY, l = 0.f;
@@ -708,7 +713,7 @@ __global__ __launch_bounds__(B) void attn_f32_kernel(
     for (int kc = 0; kc < bJ; kc += kChunk) {
       const int nk = min(kChunk, bJ - kc);
       __syncthreads();
-      for (int e = tid; e < kChunk * D; e += B) {
+      for (int e = tid; e < kChunk * D; e += 2 * B) {
         const int row = e / D;
         const size_t g = kv_off + static_cast<size_t>(kbase + kc) * D + e;
         Ks[e] = row < nk ? k[g] : 0.f;
@@ -721,8 +726,9 @@ __global__ __launch_bounds__(B) void attn_f32_kernel(
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           float acc = 0.f;
-#pragma unroll 16
-          for (int d = 0; d < D; ++d) acc = fmaf(qv[d], Ks[(j0 + j) * D + d], acc);
+#pragma unroll
+          for (int d = 0; d < DH; ++d) acc = fmaf(qv[d], Ks[(j0 + j) * D + d0 + d], acc);
+          acc += __shfl_xor(acc, 32);  // the other half of head_dim
           s[j] = j0 + j < nk ? acc : -INFINITY;
           mx = fmaxf(mx, s[j]);
         }
@@ -730,13 +736,13 @@ __global__ __launch_bounds__(B) void attn_f32_kernel(
         const float alpha = exp2f(m - m_new);
         l *= alpha;
 #pragma unroll
-        for (int d = 0; d < D; ++d) o[d] *= alpha;
+        for (int d = 0; d < DH; ++d) o[d] *= alpha;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float p = exp2f(s[j] - m_new);
           l += p;
-#pragma unroll 16
-          for (int d = 0; d < D; ++d) o[d] = fmaf(p, Vs[(j0 + j) * D + d], o[d]);
+#pragma unroll
+          for (int d = 0; d < DH; ++d) o[d] = fmaf(p, Vs[(j0 + j) * D + d0 + d], o[d]);
         }
         m = m_new;
       }
@@ -760,11 +766,11 @@ __global__ __launch_bounds__(B) void attn_f32_kernel(
       }
     }
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const float c = part != nullptr ? wb * part[row * D + d] : 0.f;
-      out[row * D + d] = fmaf(o[d], wa, c);
+    for (int d = 0; d < DH; ++d) {
+      const float c = part != nullptr ? wb * part[row * D + d0 + d] : 0.f;
+      out[row * D + d0 + d] = fmaf(o[d], wa, c);
     }
-    if (lse != nullptr) lse[row] = ls;
+    if (lse != nullptr && half == 0) lse[row] = ls;
   }
 }
 
@@ -833,7 +839,7 @@ hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const v
                        static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2, p.tokens, p.nb * B, p.nb,
                        hg.ng, hg.per_xcd);
   } else {
-    hipLaunchKernelGGL((attn_f32_kernel<D, B>), dim3(p.heads * p.nb), dim3(B), 0, stream,
+    hipLaunchKernelGGL((attn_f32_kernel<D, B>), dim3(p.heads * p.nb), dim3(2 * B), 0, stream,
                        static_cast<const float*>(q), static_cast<const float*>(k),
                        static_cast<const float*>(v), ccount, clist, head_active,
                        static_cast<const float*>(part), part_lse, static_cast<float*>(out), lse, p.tokens, p.nb,
@@ -1146,7 +1152,7 @@ hipError_t launch_cluster_attn_t(const Problem& p, const void* q, const void* k,
                        nullptr, static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2, w.Np, w.Np, w.stride,
                        hg.ng, hg.per_xcd);
   } else {
-    hipLaunchKernelGGL((attn_f32_kernel<D, B, true>), dim3(p.heads * p.nb), dim3(B), 0, stream,
+    hipLaunchKernelGGL((attn_f32_kernel<D, B, true>), dim3(p.heads * p.nb), dim3(2 * B), 0, stream,
                        static_cast<const float*>(q), reinterpret_cast<const float*>(base + w.kp_off),
                        reinterpret_cast<const float*>(base + w.vp_off), tcount, table, nullptr, nullptr, nullptr,
                        static_cast<float*>(out), lse, p.tokens, p.nb, sl2, w.Np, w.stride);
