@@ -767,8 +767,8 @@ def trajectory(wl, inp, dev, steps):
     """The 720p reuse trajectory through MaskCache.step: q and k take the
     generator's random walk, each head refreshes its mask when its drift
     passes the threshold.  Per step: the whole cache.step on the library's
-    stream (HIP events), the heads refreshed and the mean density.  The next
-    step's inputs are generated on the host while the GPU runs."""
+    stream (HIP events), the heads refreshed and the mean density.  Each
+    step's inputs are generated on the host before its timed region."""
     import numpy as np
     import torch
     import workloads as W
@@ -781,21 +781,21 @@ def trajectory(wl, inp, dev, steps):
     out = torch.empty_like(v)
     lse = torch.empty((wl.heads, wl.tokens), dtype=torch.float32, device=dev)
     rows = []
-    q, k = inp.q.to(dev), inp.k.to(dev)
     for s in range(steps):
+        # the step's inputs are generated and copied before its timed region:
+        # host work running beside the kernels delays their dispatch
+        if s > 0:
+            W.drift_step(inp, s)
+        q, k = inp.q.to(dev), inp.k.to(dev)
+        torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         cache.step(q, k, v, out=out, lse=lse)
         e1.record(stream)
-        # the next step's inputs are generated on the host while the GPU runs
-        # this one (launching first keeps host work out of the timed launches)
-        if s + 1 < steps:
-            W.drift_step(inp, s + 1)
         torch.cuda.synchronize()
         fl = cache.refresh.cpu().numpy() if s > 0 else np.ones(wl.heads, np.uint8)
         rows.append((s, float(e0.elapsed_time(e1)), fl.copy(), float(cache.density.mean().item())))
-        if s + 1 < steps:
-            q, k = inp.q.to(dev), inp.k.to(dev)
+        del q, k
         if s % 10 == 9 or s == steps - 1:
             print(json.dumps({"progress": {"trajectory_step": s, "ms": round(rows[-1][1], 3),
                                            "refreshed": int(fl.sum())}}), file=sys.stderr, flush=True)
