@@ -182,8 +182,8 @@ __device__ __forceinline__ float reduce_scatter_32(const float (&v)[16], int col
 // held as fp16 (exact for bf16 input; fp32 input adds a second fp16 term).
 // The split pooled keys stream in chunks of 32 key blocks (hi and lo tiles)
 // into a ring of NBUF LDS slots with buffer loads, shared by all waves; with
-// three slots (48 KB) three workgroups share a CU and the register budget is
-// capped to match.
+// two slots (32 KB) four workgroups share a CU, with three slots (48 KB)
+// three, and the register budget is capped to match.
 // Both passes form one walk of 2 x NBp/32 chunk steps, so the prefetch runs
 // on across the pass boundary:
 //   pass 1 (chunk steps 0..nc-1): logits S^T = Kbar Q^T (hi and lo terms in
@@ -214,7 +214,7 @@ __device__ __forceinline__ void lds_store_f32(float* p, float v) {
 // tokens (waves of block P*B/BQ + w / (BQ/32)), each with its own weight and
 // score row, so 64-token blocks still run four waves per workgroup.
 template <typename T, int D, int B, int NBUF, bool kColMask = false, int BQ = B>
-__global__ __launch_bounds__(2 * B, NBUF == 3 ? 3 : 2) void score_kernel(
+__global__ __launch_bounds__(2 * B, NBUF == 2 ? 4 : NBUF == 3 ? 3 : 2) void score_kernel(
     const T* __restrict__ q, const _Float16* __restrict__ khi, const _Float16* __restrict__ klo,
     const float* __restrict__ inv_t, const uint8_t* __restrict__ head_active,
     const int* __restrict__ colsize, float* __restrict__ scores, int N, int NB, int NBp) {
@@ -472,9 +472,10 @@ hipError_t launch_scoring_t(const Problem& p, const void* q, const void* k,
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int grid = p.heads * p.nb;
-  // bf16, 128-token blocks: a ring of three slots (48 KB), three workgroups
-  // per CU (a third wave per SIMD); fp32 queries need more registers
-  constexpr int kNbuf = std::is_same_v<T, uint16_t> ? 3 : 4;
+  // bf16 queries: a ring of two slots (32 KB, one chunk in flight), four
+  // workgroups per CU (four waves per SIMD at 128 registers); fp32 queries
+  // need more registers
+  constexpr int kNbuf = std::is_same_v<T, uint16_t> ? 2 : 4;
   if (p.block == 128)
     hipLaunchKernelGGL((score_kernel<T, D, 128, kNbuf>), dim3(grid), dim3(256), 0, stream,
                        static_cast<const T*>(q), ws.khi, ws.klo, ws.inv_t, head_active, nullptr, scores,
@@ -519,6 +520,7 @@ hipError_t launch_cluster_scoring_t(const Problem& p, const void* q, const float
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int grid = p.heads * p.nb;
+  // the empty-cluster test costs registers: three slots, three workgroups per CU
   constexpr int kNbuf = std::is_same_v<T, uint16_t> ? 3 : 4;
   if (p.block == 128)
     hipLaunchKernelGGL((score_kernel<T, D, 128, kNbuf, true>), dim3(grid), dim3(256), 0, stream,
