@@ -39,6 +39,7 @@ PEAK_HBM_GBS = 8000.0         # MI355X HBM3E peak
 WORKLOAD = "wan14b_720p"
 ATTN_PROFILE = os.path.join(ROOT, "profiles", "attn_bf16_wan14b_720p_pmc.txt")
 ATTN_SOURCE = os.path.join(ROOT, "block_sparse_attention_scoring_amd", "csrc", "attn.hip")
+TRAJ_WARM_GEMMS = 60          # bf16 8192^3 GEMMs enqueued before each timed trajectory step
 
 
 def parse():
@@ -768,7 +769,8 @@ def trajectory(wl, inp, dev, steps):
     generator's random walk, each head refreshes its mask when its drift
     passes the threshold.  Per step: the whole cache.step on the library's
     stream (HIP events), the heads refreshed and the mean density.  Each
-    step's inputs are generated on the host before its timed region."""
+    step's inputs are generated on the host before its timed region, and
+    ~50 ms of bf16 GEMMs run on the stream just before it."""
     import numpy as np
     import torch
     import workloads as W
@@ -780,6 +782,12 @@ def trajectory(wl, inp, dev, steps):
     cache = R.MaskCache(p, torch.from_numpy(inp.top_p).to(dev), wl.drift_threshold)
     out = torch.empty_like(v)
     lse = torch.empty((wl.heads, wl.tokens), dtype=torch.float32, device=dev)
+    # matrix work that keeps the GPU busy right up to each timed step, as the
+    # model's other layers would: after the seconds of host work that make a
+    # step's inputs the GPU has idled, and its clock would still be ramping up
+    wa = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    wb = torch.randn(8192, 8192, device=dev).to(torch.bfloat16)
+    wc = torch.empty(8192, 8192, dtype=torch.bfloat16, device=dev)
     rows = []
     for s in range(steps):
         # the step's inputs are generated and copied before its timed region:
@@ -788,6 +796,8 @@ def trajectory(wl, inp, dev, steps):
             W.drift_step(inp, s)
         q, k = inp.q.to(dev), inp.k.to(dev)
         torch.cuda.synchronize()
+        for _ in range(TRAJ_WARM_GEMMS):  # about 50 ms, enqueued right before the step
+            torch.matmul(wa, wb, out=wc)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         cache.step(q, k, v, out=out, lse=lse)
@@ -806,7 +816,8 @@ def trajectory(wl, inp, dev, steps):
     part = ms[1:][nref[1:] > 0]
     return {
         "workload": wl.name, "steps": steps, "drift_threshold": wl.drift_threshold,
-        "timed": "MaskCache.step (drift, gated scoring and selection, attention with the lists in force)",
+        "timed": "MaskCache.step (drift, gated scoring and selection, attention with the lists in force), "
+                 "right after ~50 ms of bf16 GEMMs on the same stream",
         "ms_step0_all_heads_refresh": round(float(ms[0]), 3),
         "ms_reuse_step_mean": round(float(reuse.mean()), 3) if reuse.size else None,
         "reuse_steps": int(reuse.size),
