@@ -277,7 +277,9 @@ __global__ __launch_bounds__(256) void vt_kernel(const uint16_t* __restrict__ v,
   const size_t np = static_cast<size_t>(NB) * B;
   for (int c = tid; c < B * D / 8; c += 256) {
     const int r = c / (D / 8), c8 = c % (D / 8);
-    u32x4 x = r < bJ ? *reinterpret_cast<const u32x4*>(v + (static_cast<size_t>(h) * N + kbase + r) * D + c8 * 8)
+    // (non-temporal: V is read once)
+    u32x4 x = r < bJ ? __builtin_nontemporal_load(
+                           reinterpret_cast<const u32x4*>(v + (static_cast<size_t>(h) * N + kbase + r) * D + c8 * 8))
                      : u32x4{0, 0, 0, 0};
 #pragma unroll
     for (int e = 0; e < 4; ++e) {

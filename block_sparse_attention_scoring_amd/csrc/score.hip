@@ -56,6 +56,33 @@ __device__ __forceinline__ void load8<float>(const float* src, float (&x)[8]) {
   }
 }
 
+// The same with a non-temporal load, for the pooling pass's read-once
+// stream over K (the scorer's query loads keep the default policy, which
+// measured faster there).
+template <typename T>
+__device__ __forceinline__ void load8_nt(const T* src, float (&x)[8]);
+
+template <>
+__device__ __forceinline__ void load8_nt<uint16_t>(const uint16_t* src, float (&x)[8]) {
+  const u32x4 raw = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(src));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[2 * e] = __uint_as_float(raw[e] << 16);
+    x[2 * e + 1] = __uint_as_float(raw[e] & 0xffff0000u);
+  }
+}
+
+template <>
+__device__ __forceinline__ void load8_nt<float>(const float* src, float (&x)[8]) {
+  const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src));
+  const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(src + 4));
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    x[e] = a[e];
+    x[4 + e] = b[e];
+  }
+}
+
 // ---------------------------------------------------------------- pool
 template <typename T, int D>
 __global__ __launch_bounds__(kPoolThreads) void pool_kernel(
@@ -74,7 +101,7 @@ __global__ __launch_bounds__(kPoolThreads) void pool_kernel(
   double acc[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   for (int r = rg; r < bJ; r += kRowsPerPass) {
     float x[8];
-    load8<T>(src + static_cast<size_t>(r) * D, x);
+    load8_nt<T>(src + static_cast<size_t>(r) * D, x);
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[e] += static_cast<double>(x[e]);
   }
