@@ -97,15 +97,223 @@ __global__ __launch_bounds__(256) void canon_kernel(const int* __restrict__ coun
   if (tid == 0) ccount[row] = base;
 }
 
-// Pair lists for 64-token blocks.  One workgroup per (pair P, head h): the
-// lists of query blocks 2P and 2P+1, read as sets like canon_kernel reads
-// them, are marked in two LDS byte maps; the union is compacted in
-// ascending order, each entry J | (bits << 16) where bit 0 / bit 1 says
-// that block 2P / 2P+1 lists J.  With `complement` set each row's blocks not
-// listed are taken instead.  Heads with head_active[h] == 0 are skipped.
+// ---------------------------------------------------------------- pairing
+// 64-token blocks run in pairs, one 128-row workgroup walking the union of
+// two blocks' key sets, and a wave idles on the key blocks only its partner
+// selected.  So a pair costs the size of the symmetric difference of its two
+// sets on top of their own work, and the pairs are chosen to keep that
+// small: each block may pair with the kPairWin blocks on either side (in the
+// (frame, height, width) token order this reaches the same place in the
+// neighbouring frame for a 21 x 30 x 52 latent: 24.4 blocks per frame),
+// inside segments of kPairSeg blocks.  The matching is the greedy one
+// (lightest edge first, ties by the lower block and then the shorter
+// distance), computed in rounds: every unmatched block proposes its
+// lightest edge to an unmatched block, and mutual proposals are matched.
+// After kPairRounds rounds the blocks left without a partner are paired in
+// ascending order; only the last segment can leave one block alone.  The
+// pairs change which blocks share a workgroup, not what any query sees:
+// each block still walks its own set in ascending order.
+constexpr int kPairWin = 32;     // candidate partners on each side
+constexpr int kPairSeg = 128;    // blocks matched together (one workgroup, one per thread)
+constexpr int kPairRounds = 8;   // rounds before the rest is paired in order
+static_assert(kPairSeg == 128 && kPairWin == 32, "key packing: weight (13 bits), block (7), distance (5)");
+
+// One workgroup per (row, head): the row's set (as canon_kernel reads it,
+// complement applied) as NW = ceil(NB / 64) words of bits.
+__global__ __launch_bounds__(256) void pair_bits_kernel(const int* __restrict__ counts,
+                                                        const int* __restrict__ block_idx,
+                                                        const uint8_t* __restrict__ head_active,
+                                                        int complement, uint64_t* __restrict__ bits, int NB) {
+  __shared__ uint8_t mark[kMaxNB];
+  const int I = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
+  if (head_active != nullptr && head_active[h] == 0) return;
+  const int lane = tid & 63, wave = tid >> 6;
+  const size_t row = static_cast<size_t>(h) * NB + I;
+  for (int e = tid; e < NB; e += 256) mark[e] = 0;
+  __syncthreads();
+  const int c = min(max(counts[row], 0), NB);
+  for (int t = tid; t < c; t += 256) {
+    const int j = block_idx[row * NB + t];
+    if (static_cast<unsigned>(j) < static_cast<unsigned>(NB)) mark[j] = 1;
+  }
+  __syncthreads();
+  const int nw = (NB + 63) / 64;
+  for (int w = wave; w < nw; w += 4) {
+    const int e = 64 * w + lane;
+    const uint64_t b = __ballot(e < NB && (mark[e] != 0) != (complement != 0));
+    if (lane == 0) bits[row * nw + w] = b;
+  }
+}
+
+// One wave per (row i, head): lane t < kPairWin writes the symmetric
+// difference of rows i and i + 1 + t (0xffff when that row is past the end
+// or in the next segment).
+__global__ __launch_bounds__(64) void pair_weight_kernel(const uint64_t* __restrict__ bits,
+                                                         const uint8_t* __restrict__ head_active,
+                                                         uint16_t* __restrict__ wtab, int NB) {
+  const int i = blockIdx.x, h = blockIdx.y, t = threadIdx.x;
+  if (head_active != nullptr && head_active[h] == 0) return;
+  if (t >= kPairWin) return;
+  const int j = i + 1 + t, nw = (NB + 63) / 64;
+  int w = 0xffff;
+  if (j < NB && j / kPairSeg == i / kPairSeg) {
+    const uint64_t* a = bits + (static_cast<size_t>(h) * NB + i) * nw;
+    const uint64_t* b = bits + (static_cast<size_t>(h) * NB + j) * nw;
+    w = 0;
+    for (int k = 0; k < nw; ++k) w += __builtin_popcountll(a[k] ^ b[k]);
+  }
+  wtab[(static_cast<size_t>(h) * NB + i) * kPairWin + t] = static_cast<uint16_t>(w);
+}
+
+// Exclusive rank of `f` over the workgroup's kPairSeg threads, and the total.
+__device__ __forceinline__ int rank_seg(bool f, int* wsum, int* total) {
+  constexpr int kW = kPairSeg / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const uint64_t bal = __ballot(f);
+  if (lane == 0) wsum[wave] = __builtin_popcountll(bal);
+  __syncthreads();
+  int off = 0, tot = 0;
+#pragma unroll
+  for (int w = 0; w < kW; ++w) {
+    off += w < wave ? wsum[w] : 0;
+    tot += wsum[w];
+  }
+  __syncthreads();
+  *total = tot;
+  return off + __builtin_popcountll(bal & ((1ull << lane) - 1));
+}
+
+// One workgroup per (segment, head), thread r holding block s0 + r of the
+// segment.  Edge keys: weight << 12 | lower block << 5 | distance - 1,
+// unique per edge, so the lightest edge of the rest is always mutual and
+// every round matches at least one pair.  Output: unit P of the head holds
+// blocks pairs[P].x < pairs[P].y (y = -1: a block alone), units in order of
+// their first block, (NB + 1) / 2 of them.
+__global__ __launch_bounds__(kPairSeg) void pair_match_kernel(const uint16_t* __restrict__ wtab,
+                                                              const uint8_t* __restrict__ head_active,
+                                                              int2* __restrict__ pairs, int NB) {
+  constexpr int kWords = kPairSeg / 32 + 3;  // taken bits: 32 guard bits, the segment, 64 guard bits
+  constexpr int kW = kPairSeg / 64;
+  __shared__ uint16_t wf_s[kPairSeg][kPairWin];  // forward weights of each block
+  __shared__ int st[kPairSeg];                   // partner (index in the segment), -1 unmatched, -2 none
+  __shared__ uint32_t best[kPairSeg];            // proposal of each block
+  __shared__ uint32_t taken[kWords];             // bit 32 + k: block k is matched or absent
+  __shared__ int idx[kPairSeg];                  // leftover of each rank
+  __shared__ int wsum[kW];
+  __shared__ int anyw[kW];
+  const int s0 = blockIdx.x * kPairSeg, h = blockIdx.y, r = threadIdx.x, lane = r & 63, wave = r >> 6;
+  if (head_active != nullptr && head_active[h] == 0) return;
+  const int units = (NB + 1) / 2, n = min(kPairSeg, NB - s0);
+  const bool live = r < n;
+  constexpr uint32_t kNone = 0xffffffffu;
+  // this block's edge weights, two per register: forward to block r + 1 + t,
+  // backward from block r - 1 - t (0xffff: no edge); then its edge keys
+  uint32_t fw[kPairWin / 2];
+  uint32_t fk[kPairWin], bk[kPairWin];
+  {
+    const u32x4* src = reinterpret_cast<const u32x4*>(wtab + (static_cast<size_t>(h) * NB + s0 + (live ? r : 0)) *
+                                                                 kPairWin);
+#pragma unroll
+    for (int c = 0; c < kPairWin / 8; ++c) {
+      const u32x4 x = live ? src[c] : u32x4{kNone, kNone, kNone, kNone};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) fw[4 * c + e] = x[e];
+    }
+#pragma unroll
+    for (int t = 0; t < kPairWin; t += 2)
+      *reinterpret_cast<uint32_t*>(&wf_s[r][t]) = fw[t / 2];
+  }
+  st[r] = live ? -1 : -2;
+  best[r] = kNone;
+  if (r == 0) taken[0] = kNone;              // the 32 blocks before the segment
+  if (r < 2) taken[kWords - 2 + r] = kNone;  // the 64 after it
+  // lane 0 of each wave publishes which of its blocks are taken
+  auto publish = [&](bool tk) {
+    const uint64_t m = __ballot(tk);
+    if (lane == 0) {
+      taken[1 + 2 * wave] = static_cast<uint32_t>(m);
+      taken[2 + 2 * wave] = static_cast<uint32_t>(m >> 32);
+    }
+  };
+  publish(!live);
+  __syncthreads();
+  auto key = [&](uint32_t w, int a, int t) {
+    return w == 0xffffu ? kNone : (w << 12) | (static_cast<uint32_t>(a) << 5) | static_cast<uint32_t>(t);
+  };
+#pragma unroll
+  for (int t = 0; t < kPairWin; ++t) {
+    fk[t] = key((fw[t / 2] >> ((t & 1) * 16)) & 0xffffu, r, t);
+    bk[t] = key(live && r - 1 - t >= 0 ? wf_s[r - 1 - t][t] : 0xffffu, r - 1 - t, t);
+  }
+  for (int round = 0; round < kPairRounds; ++round) {
+    // proposals, recomputed when the block proposed to has been taken
+    if (st[r] == -1) {
+      uint32_t b = best[r];
+      bool stale = b == kNone;
+      if (!stale) {
+        const int a = (b >> 5) & (kPairSeg - 1);
+        stale = st[a == r ? a + 1 + static_cast<int>(b & 31) : a] != -1;
+      }
+      if (stale) {
+        const int pf = r + 33, pb = r;  // bit positions of blocks r + 1 and r - 32
+        const uint64_t wfv = (static_cast<uint64_t>(taken[pf / 32 + 1]) << 32) | taken[pf / 32];
+        const uint64_t wbv = (static_cast<uint64_t>(taken[pb / 32 + 1]) << 32) | taken[pb / 32];
+        const uint32_t tf = static_cast<uint32_t>(wfv >> (pf & 31));  // bit t: block r + 1 + t
+        const uint32_t tb = static_cast<uint32_t>(wbv >> (pb & 31));  // bit 31 - t: block r - 1 - t
+        b = kNone;
+#pragma unroll
+        for (int t = 0; t < kPairWin; ++t) {
+          b = min(b, ((tf >> t) & 1u) ? kNone : fk[t]);
+          b = min(b, ((tb >> (31 - t)) & 1u) ? kNone : bk[t]);
+        }
+        best[r] = b;
+      }
+    }
+    __syncthreads();
+    bool matched = false;
+    if (st[r] == -1 && best[r] != kNone) {
+      const uint32_t b = best[r];
+      const int a = (b >> 5) & (kPairSeg - 1), o = a == r ? a + 1 + static_cast<int>(b & 31) : a;
+      if (best[o] == b) {
+        st[r] = o;
+        matched = true;
+      }
+    }
+    publish(st[r] != -1);
+    const uint64_t mm = __ballot(matched);
+    if (lane == 0) anyw[wave] = mm != 0;
+    __syncthreads();
+    int any = 0;
+#pragma unroll
+    for (int w = 0; w < kW; ++w) any |= anyw[w];
+    if (any == 0) break;
+  }
+  // the rest in ascending order: ranks 2m and 2m + 1 pair up
+  int nleft;
+  const bool left = st[r] == -1;
+  const int rk = rank_seg(left, wsum, &nleft);
+  if (left) idx[rk] = r;
+  __syncthreads();
+  if (left) st[r] = (rk & 1) ? idx[rk - 1] : rk + 1 < nleft ? idx[rk + 1] : -2;
+  __syncthreads();
+  int nunits;
+  const bool lead = live && (st[r] > r || st[r] == -2);
+  const int P = s0 / 2 + rank_seg(lead, wsum, &nunits);
+  if (lead && P < units)
+    pairs[static_cast<size_t>(h) * units + P] = make_int2(s0 + r, st[r] >= 0 ? s0 + st[r] : -1);
+}
+
+// Pair lists for 64-token blocks.  One workgroup per (unit P, head h): the
+// lists of the unit's blocks a = pairs[P].x and b = pairs[P].y (pair_match_kernel;
+// b = -1: a alone), read as sets like canon_kernel reads them, are marked in
+// two LDS byte maps; the union is compacted in ascending order, each entry
+// J | (bits << 16) where bit 0 / bit 1 says that block a / b lists J.  With
+// `complement` set each row's blocks not listed are taken instead.  Heads
+// with head_active[h] == 0 are skipped.
 __global__ __launch_bounds__(256) void pair_canon_kernel(const int* __restrict__ counts,
                                                          const int* __restrict__ block_idx,
                                                          const uint8_t* __restrict__ head_active,
+                                                         const int2* __restrict__ pairs,
                                                          int complement, int* __restrict__ ccount,
                                                          int* __restrict__ clist, int NB) {
   __shared__ uint8_t mark0[kMaxNB];
@@ -119,9 +327,10 @@ __global__ __launch_bounds__(256) void pair_canon_kernel(const int* __restrict__
     mark1[e] = 0;
   }
   __syncthreads();
-  const int nrows = min(2, NB - 2 * P);  // the last pair may hold one block
+  const int2 pr = pairs[static_cast<size_t>(h) * ((NB + 1) / 2) + P];
+  const int nrows = pr.y >= 0 ? 2 : 1;
   for (int q = 0; q < nrows; ++q) {
-    const size_t row = static_cast<size_t>(h) * NB + 2 * P + q;
+    const size_t row = static_cast<size_t>(h) * NB + (q == 0 ? pr.x : pr.y);
     uint8_t* mk = q == 0 ? mark0 : mark1;
     const int c = min(max(counts[row], 0), NB);
     for (int t = tid; t < c; t += 256) {
@@ -319,16 +528,17 @@ __global__ __launch_bounds__(256) void vt_kernel(const uint16_t* __restrict__ v,
 // layout holding (e & 31) + 1 real keys; K has Nk rows and V^T Nv columns per
 // head.  Every sub-tile may be partial, so each step applies its mask.
 //
-// BQ < B (pair mode, BQ = B/2 = 64): the workgroup serves query blocks 2P and
-// 2P+1 of BQ tokens (waves 0-1 and 2-3) over the union of their lists
-// (pair_canon_kernel); each wave skips the sub-tiles its own block did not
-// select.  Each SIMD's waves still come from different workgroups.
+// BQ < B (pair mode, BQ = B/2 = 64): the workgroup serves the two query
+// blocks of BQ tokens of a unit (pair_match_kernel; waves 0-1 and 2-3) over
+// the union of their lists (pair_canon_kernel); each wave skips the
+// sub-tiles its own block did not select.  Each SIMD's waves still come from different workgroups.
 template <int D, int B, int KS, int NBUF, bool kTable = false, int BQ = B>
 __global__ __launch_bounds__(2 * B, NBUF == 3 ? 3 : 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
     const uint16_t* __restrict__ vt, const int* __restrict__ ccount,
     const int* __restrict__ clist, const uint8_t* __restrict__ head_active, const int* __restrict__ perm,
-    const uint16_t* part, const float* part_lse, uint16_t* out, float* lse, int H, int N, int NB,
+    const int2* __restrict__ pairs, const uint16_t* part, const float* part_lse, uint16_t* out, float* lse, int H,
+    int N, int NB,
     float scale_log2, int Nk, int Nv, int lstride, int ng, int per_xcd) {
   using S = AttnShape<D, B, KS, NBUF>;
   static_assert(NBUF >= 3 && NBUF <= 4, "ring of 3 or 4 LDS slots");
@@ -364,7 +574,14 @@ __global__ __launch_bounds__(2 * B, NBUF == 3 ? 3 : 2) void attn_bf16_kernel(
   const int hl = lane >> 5, col = lane & 31;
   const size_t head_off = static_cast<size_t>(h) * N * D;
   const size_t np = static_cast<size_t>(Nv);
-  const int qrow = kPair ? (2 * I + (wave >> 1)) * BQ + (wave & 1) * 32 + col : I * B + wave * 32 + col;
+  // pair mode: waves 0-1 hold block pairs[I].x, waves 2-3 block pairs[I].y
+  // (none: y = -1, taken as block NB, whose rows all lie past the end)
+  int qblk = I;
+  if constexpr (kPair) {
+    const int2 pr = pairs[static_cast<size_t>(h) * units + I];
+    qblk = (wave >> 1) == 0 ? pr.x : pr.y >= 0 ? pr.y : NB;
+  }
+  const int qrow = kPair ? qblk * BQ + (wave & 1) * 32 + col : I * B + wave * 32 + col;
   const int mbit = kPair ? 1 << (wave >> 1) : 0;  // this wave's bit in a pair entry
 
   bf16x8 qf[S::kKSD];
@@ -779,7 +996,7 @@ __global__ __launch_bounds__(2 * B) void attn_f32_kernel(
 // Attention workspace: [V^T (bf16 only)][canonical counts][canonical lists],
 // each part 256-byte aligned.
 struct AttnWs {
-  size_t ccount_off, clist_off, perm_off, total;
+  size_t ccount_off, clist_off, perm_off, pairs_off, bits_off, wtab_off, total;
 };
 
 AttnWs attn_ws_layout(const Problem& p) {
@@ -791,7 +1008,13 @@ AttnWs attn_ws_layout(const Problem& p) {
   w.perm_off = w.clist_off + al(sizeof(int) * rows * p.nb);
   // dispatch order (bf16 path): per head group 8 eighths of its units
   const HeadGroups hg = head_groups(p, p.block == 64 ? (p.nb + 1) / 2 : p.nb);
-  w.total = w.perm_off + (p.dtype == 0 ? al(sizeof(int) * 8 * static_cast<size_t>(hg.ng) * hg.per_xcd) : 0);
+  w.pairs_off = w.perm_off + (p.dtype == 0 ? al(sizeof(int) * 8 * static_cast<size_t>(hg.ng) * hg.per_xcd) : 0);
+  // pairing of 64-token blocks (bf16): the pairs, the rows' bit sets, the edge weights
+  const bool pairs = p.dtype == 0 && p.block == 64;
+  const size_t nw = (static_cast<size_t>(p.nb) + 63) / 64;
+  w.bits_off = w.pairs_off + (pairs ? al(sizeof(int2) * p.heads * ((static_cast<size_t>(p.nb) + 1) / 2)) : 0);
+  w.wtab_off = w.bits_off + (pairs ? al(sizeof(uint64_t) * rows * nw) : 0);
+  w.total = w.wtab_off + (pairs ? al(sizeof(uint16_t) * rows * kPairWin) : 0);
   return w;
 }
 
@@ -807,10 +1030,18 @@ hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const v
   int* clist = reinterpret_cast<int*>(base + w.clist_off);
   // 64-token blocks on the matrix cores: pairs of query blocks per workgroup
   constexpr bool kPairs = B == 64;
-  if (p.dtype == 0 && kPairs)
+  int2* pairs = reinterpret_cast<int2*>(base + w.pairs_off);
+  if (p.dtype == 0 && kPairs) {
+    uint64_t* bits = reinterpret_cast<uint64_t*>(base + w.bits_off);
+    uint16_t* wtab = reinterpret_cast<uint16_t*>(base + w.wtab_off);
+    hipLaunchKernelGGL(pair_bits_kernel, dim3(p.nb, p.heads), dim3(256), 0, stream, counts, idx, head_active,
+                       complement, bits, p.nb);
+    hipLaunchKernelGGL(pair_weight_kernel, dim3(p.nb, p.heads), dim3(64), 0, stream, bits, head_active, wtab, p.nb);
+    hipLaunchKernelGGL(pair_match_kernel, dim3((p.nb + kPairSeg - 1) / kPairSeg, p.heads), dim3(kPairSeg), 0, stream,
+                       wtab, head_active, pairs, p.nb);
     hipLaunchKernelGGL(pair_canon_kernel, dim3((p.nb + 1) / 2, p.heads), dim3(256), 0, stream, counts, idx,
-                       head_active, complement, ccount, clist, p.nb);
-  else
+                       head_active, pairs, complement, ccount, clist, p.nb);
+  } else
     hipLaunchKernelGGL(canon_kernel, dim3(p.nb, p.heads), dim3(256), 0, stream, counts, idx, head_active,
                        complement, ccount, clist, p.nb);
   hipError_t e = hipGetLastError();
@@ -837,9 +1068,9 @@ hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const v
     const int grid = 8 * hg.per_xcd * hg.ng;
     hipLaunchKernelGGL((attn_bf16_kernel<D, kRows, kKs, kNbuf, false, B>), dim3(grid), dim3(S::kThreads), 0,
                        stream, static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k), vt, ccount,
-                       clist, head_active, perm, static_cast<const uint16_t*>(part), part_lse,
-                       static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2, p.tokens, p.nb * B, p.nb,
-                       hg.ng, hg.per_xcd);
+                       clist, head_active, perm, kPairs ? pairs : nullptr, static_cast<const uint16_t*>(part),
+                       part_lse, static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2, p.tokens, p.nb * B,
+                       p.nb, hg.ng, hg.per_xcd);
   } else {
     hipLaunchKernelGGL((attn_f32_kernel<D, B>), dim3(p.heads * p.nb), dim3(2 * B), 0, stream,
                        static_cast<const float*>(q), static_cast<const float*>(k),
@@ -1151,7 +1382,7 @@ hipError_t launch_cluster_attn_t(const Problem& p, const void* q, const void* k,
     hipLaunchKernelGGL((attn_bf16_kernel<D, B, 32, kNbuf, true>), dim3(grid), dim3(S::kThreads), 0, stream,
                        static_cast<const uint16_t*>(q), reinterpret_cast<const uint16_t*>(base + w.kp_off),
                        reinterpret_cast<const uint16_t*>(base + w.vp_off), tcount, table, nullptr, perm, nullptr,
-                       nullptr, static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2, w.Np, w.Np, w.stride,
+                       nullptr, nullptr, static_cast<uint16_t*>(out), lse, p.heads, p.tokens, p.nb, sl2, w.Np, w.Np, w.stride,
                        hg.ng, hg.per_xcd);
   } else {
     hipLaunchKernelGGL((attn_f32_kernel<D, B, true>), dim3(p.heads * p.nb), dim3(2 * B), 0, stream,

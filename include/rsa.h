@@ -226,11 +226,14 @@ rsa_status rsa_mask_drift(const rsa_problem* p, const void* q, const void* k,
  *   aligned, each part rounded up to 256 bytes: (bf16 only) v re-laid out
  *   key-major for the matrix cores, heads * head_dim * NB * block * 2 bytes;
  *   then every row's list in canonical form (ascending, no repeats, no
- *   invalid entries; bf16 with block 64: the union of query blocks 2P and
- *   2P+1 per pair, with membership bits): counts, heads * NB * 4 bytes, and
+ *   invalid entries; bf16 with block 64: per pair of query blocks the union
+ *   of their lists, with membership bits): counts, heads * NB * 4 bytes, and
  *   lists, heads * NB * NB * 4 bytes; then (bf16 only) the workgroup
  *   dispatch order, 4 bytes per query block (per pair of 64-token blocks)
- *   plus padding to whole eighths of each head group.
+ *   plus padding to whole eighths of each head group; then (bf16 with block
+ *   64 only) the pairing of query blocks: the pairs, heads * ceil(NB/2) * 8
+ *   bytes, each row's set as bits, heads * NB * ceil(NB/64) * 8 bytes, and
+ *   the overlap of each block with its 32 successors, heads * NB * 64 bytes.
  * Non-finite values in q, k or v give undefined results.
  */
 rsa_status rsa_block_sparse_attn(const rsa_problem* p, const void* q, const void* k,

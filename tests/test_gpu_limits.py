@@ -9,7 +9,8 @@ Scores of sampled query blocks against the fp64 oracle.  Attention on hand-made
 lists: a full row (all 4096 blocks, shuffled), an empty row, the ragged last
 block alone, a row with repeats and out-of-range entries, its pair partner
 with a different list, a 3000-block row and short random rows elsewhere;
-sampled rows against the oracle on the same (cleaned) lists.
+sampled rows against the oracle on the same (cleaned) lists; every row is
+checked to be written, and empty exactly when its cleaned list is.
 """
 import sys
 
@@ -82,9 +83,18 @@ def test_largest_problem(name):
 
     S = R.score_blocks(q, k, p)
     counts, idx, rows = make_lists(rng, NB)
+    # NaN-filled outputs: a row no workgroup writes (64-token blocks: a block
+    # left out of every pair) keeps its NaN
+    out0 = torch.full_like(q, float("nan"))
+    lse0 = torch.full((1, tokens), float("nan"), dtype=torch.float32, device=DEV)
     out, lse = R.block_sparse_attn(q, k, v, torch.from_numpy(counts[None]).to(DEV),
-                                   torch.from_numpy(idx[None]).to(DEV), p)
+                                   torch.from_numpy(idx[None]).to(DEV), p, out=out0, lse=lse0)
     torch.cuda.synchronize()
+    # every row: written, and empty exactly when its list has no valid entry
+    l_all = host(lse[0])
+    assert not np.isnan(l_all).any() and not torch.isnan(out).any().item()
+    has = np.array([clean(idx[i, :counts[i]], NB).size > 0 for i in range(NB)])
+    assert (np.isneginf(l_all) == np.repeat(~has, b)[:tokens]).all()
     q64, k64, v64 = W.to_f64(inp.q[0]), W.to_f64(inp.k[0]), W.to_f64(inp.v[0])
     scale = 1.0 / np.sqrt(d)
 
