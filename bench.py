@@ -665,12 +665,11 @@ def main():
 
 def attn_kernel_name(wl):
     """The attention kernel instantiation a workload launches (csrc/attn.hip):
-    128 query rows per workgroup, 32-key sub-tiles; 128-token blocks keep a
-    three-slot ring, 64-token blocks run in pairs with a four-slot ring."""
+    128 query rows per workgroup, 32-key sub-tiles and a three-slot ring;
+    64-token blocks run in pairs."""
     if wl.dtype != "bf16":
         return f"attn_f32_kernel<{wl.head_dim},{wl.block}>"
-    nbuf = 4 if wl.block == 64 else 3
-    return f"attn_bf16_kernel<{wl.head_dim},128,32,{nbuf},false,{wl.block}>"
+    return f"attn_bf16_kernel<{wl.head_dim},128,32,3,false,{wl.block}>"
 
 
 def measure(wl, inp, dev, steps, warmup):

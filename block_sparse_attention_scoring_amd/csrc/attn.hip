@@ -531,7 +531,8 @@ __global__ __launch_bounds__(256) void vt_kernel(const uint16_t* __restrict__ v,
 // BQ < B (pair mode, BQ = B/2 = 64): the workgroup serves the two query
 // blocks of BQ tokens of a unit (pair_match_kernel; waves 0-1 and 2-3) over
 // the union of their lists (pair_canon_kernel); each wave skips the
-// sub-tiles its own block did not select.  Each SIMD's waves still come from different workgroups.
+// sub-tiles its own block did not select.  Each SIMD's waves still come
+// from different workgroups.
 template <int D, int B, int KS, int NBUF, bool kTable = false, int BQ = B>
 __global__ __launch_bounds__(2 * B, NBUF == 3 ? 3 : 2) void attn_bf16_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
@@ -746,6 +747,31 @@ __global__ __launch_bounds__(2 * B, NBUF == 3 ? 3 : 2) void attn_bf16_kernel(
       for (int w = 0; w < S::kKSK; ++w) oacc[dt] = mfma32(a[w], pb[w], oacc[dt]);
     }
   };
+  // pv in two parts for pair mode: P and its row sums (pexp), then the
+  // products (pvm)
+  auto pexp = [&](const f32x16* sacc, bf16x8* pb) {
+#pragma unroll
+    for (int t = 0; t < S::kKT; ++t) {
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[t][r], scale_log2, -m_run));
+        l_part[r & 3] += p;
+        pb[2 * t + (r >> 3)][r & 7] = static_cast<__bf16>(p);
+      }
+    }
+  };
+  auto pvm = [&](const bf16x8* pb, const uint16_t* cur) {
+    const char* vs = reinterpret_cast<const char*>(cur + S::kTile);
+#pragma unroll
+    for (int dt = 0; dt < S::kDT; ++dt) {
+      bf16x8 a[S::kKSK];
+#pragma unroll
+      for (int w = 0; w < S::kKSK; ++w)
+        a[w] = *reinterpret_cast<const bf16x8*>(vs + dt * (32 * 2 * KS) + vlane[w]);
+#pragma unroll
+      for (int w = 0; w < S::kKSK; ++w) oacc[dt] = mfma32(a[w], pb[w], oacc[dt]);
+    }
+  };
   auto ring = [&](int i) { return i == 0 ? slot0 : i == 1 ? slot1 : i == 2 ? slot2 : slot3; };
 
   // Sub-tile u lives in ring slot u % NBUF.  Software pipeline over the
@@ -796,22 +822,19 @@ __global__ __launch_bounds__(2 * B, NBUF == 3 ? 3 : 2) void attn_bf16_kernel(
         mprev = rowmax(sprev);
       } else {
         // the single-block step with each half skipped where this wave's
-        // block did not select the sub-tile (wave-uniform branches)
+        // block did not select the sub-tile (wave-uniform branches).  The
+        // exponentials of sub-tile j-1 come first, so its scores are dead
+        // before S^T of sub-tile j is written into the same registers: the
+        // step fits the three-workgroup register budget without spills.
         const bool mc = member(jj);
         if (pvalid) rescale(mprev);
         wait_vm<(NBUF - 3) * kPer>();
         barrier_lds();
         issue(jj + NBUF - 2, fill);
-        f32x16 scur[S::kKT];
-        if (mc) {
-          qk(kslot, scur);
-        } else {
-#pragma unroll
-          for (int t = 0; t < S::kKT; ++t) scur[t] = f32x16{} - INFINITY;
-        }
-        if (pvalid) pv(sprev, vslot);
-#pragma unroll
-        for (int t = 0; t < S::kKT; ++t) sprev[t] = scur[t];
+        bf16x8 pb[S::kKSK];
+        if (pvalid) pexp(sprev, pb);
+        if (mc) qk(kslot, sprev);
+        if (pvalid) pvm(pb, vslot);
         if (mc) mprev = rowmax(sprev);
         pvalid = mc;
       }
@@ -1047,10 +1070,9 @@ hipError_t launch_attn_t(const Problem& p, const void* q, const void* k, const v
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.dtype == 0) {
-    // Single blocks: a ring of three 32-key sub-tiles, three workgroups per
-    // CU.  Pairs keep four slots and two workgroups per CU: at the
-    // three-wave register budget their skip logic spills.
-    constexpr int kKs = RSA_ATTN_KS, kNbuf = kPairs ? 4 : RSA_ATTN_NBUF;
+    // A ring of three 32-key sub-tiles, three workgroups per CU (single
+    // blocks and pairs alike).
+    constexpr int kKs = RSA_ATTN_KS, kNbuf = RSA_ATTN_NBUF;
     constexpr int kRows = 128;  // query rows per workgroup (a block, or a pair of 64-token blocks)
     using S = AttnShape<D, kRows, kKs, kNbuf>;
     uint16_t* vt = reinterpret_cast<uint16_t*>(base);
