@@ -687,11 +687,17 @@ __global__ __launch_bounds__(2 * B, NBUF == 3 ? 3 : 2) void attn_bf16_kernel(
   auto mask_tail = [&](int u, f32x16* sacc) {
     const int valid = kTable ? (list[u] & 31) + 1 : N - sub_base(u);
     if (valid < KS) {
+      // register r of tile t holds key 32t + acc_row(r, 0) + 4 hl: whether it
+      // lies past the end is uniform in each lane half, so the condition is a
+      // lane mask built in scalar registers (no per-lane value kept live)
 #pragma unroll
       for (int t = 0; t < S::kKT; ++t)
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * t + acc_row(r, hl) >= valid) sacc[t][r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int c = 32 * t + acc_row(r, 0);
+          const uint64_t m = (c >= valid ? 0xffffffffull : 0ull) | (c + 4 >= valid ? 0xffffffff00000000ull : 0ull);
+          if (__builtin_amdgcn_inverse_ballot_w64(m)) sacc[t][r] = -INFINITY;
+        }
     }
   };
   // maximum of this query's scores in the sub-tile, log2 units; the two
@@ -1390,9 +1396,9 @@ hipError_t launch_cluster_attn_t(const Problem& p, const void* q, const void* k,
                      tcount, table, p.nb, w.stride);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.dtype == 0) {
-    // four slots for 128-token rows: the sub-tile masks do not fit the
-    // three-wave register budget
-    constexpr int kNbuf = B == 128 ? 4 : 3;
+    // three slots, three workgroups per CU (the sub-tile masks are built in
+    // scalar registers, so they fit the three-wave register budget)
+    constexpr int kNbuf = 3;
     using S = AttnShape<D, B, 32, kNbuf>;
     const HeadGroups hg = head_groups(p, p.nb);
     int* perm = reinterpret_cast<int*>(base + w.perm_off);
