@@ -391,13 +391,22 @@ __global__ __launch_bounds__(2 * B, NBUF == 2 ? 4 : NBUF == 3 ? 3 : 2) void scor
       if constexpr (kColMask) {
         // lane col's bit says whether column 32u + col is a live cluster
         const uint32_t live = static_cast<uint32_t>(__ballot(live_col(u)));
+        // register r holds column acc_row(r, 0) + 4 hl: its test is uniform in
+        // each lane half, so it is a lane mask built in scalar registers
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (!((live >> acc_row(r, hl)) & 1u)) acc[r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int c = acc_row(r, 0);
+          const uint64_t m = (((live >> c) & 1u) ? 0ull : 0xffffffffull) |
+                             (((live >> (c + 4)) & 1u) ? 0ull : 0xffffffff00000000ull);
+          if (__builtin_amdgcn_inverse_ballot_w64(m)) acc[r] = -INFINITY;
+        }
       } else if (32 * u + 32 > NB) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r)
-          if (32 * u + acc_row(r, hl) >= NB) acc[r] = -INFINITY;
+        for (int r = 0; r < 16; ++r) {
+          const int c = 32 * u + acc_row(r, 0);
+          const uint64_t m = (c >= NB ? 0xffffffffull : 0ull) | (c + 4 >= NB ? 0xffffffff00000000ull : 0ull);
+          if (__builtin_amdgcn_inverse_ballot_w64(m)) acc[r] = -INFINITY;
+        }
       }
       float cm = -INFINITY;
 #pragma unroll
@@ -547,8 +556,8 @@ hipError_t launch_cluster_scoring_t(const Problem& p, const void* q, const float
   e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int grid = p.heads * p.nb;
-  // the empty-cluster test costs registers: three slots, three workgroups per CU
-  constexpr int kNbuf = std::is_same_v<T, uint16_t> ? 3 : 4;
+  // bf16 queries: two slots, four workgroups per CU, as for key blocks
+  constexpr int kNbuf = std::is_same_v<T, uint16_t> ? 2 : 4;
   if (p.block == 128)
     hipLaunchKernelGGL((score_kernel<T, D, 128, kNbuf, true>), dim3(grid), dim3(256), 0, stream,
                        static_cast<const T*>(q), ws.khi, ws.klo, ws.inv_t, nullptr, sizes, scores, p.tokens,
