@@ -122,12 +122,14 @@ __global__ __launch_bounds__(256) void gram_reduce_kernel(const float* __restric
 // For 32 centroids per workgroup: W_j = 2 G c_j (fp32) and b_j = c_j . (G c_j);
 // W_j times its own power of two t_j (max |W_j t_j| in [2^13, 2^14)) split
 // into fp16 hi + lo, 22 significant bits, and 1 / t_j.  Rows past NB get zero
-// W and b = +inf, so they never win the assignment.
+// W and b = +inf, so they never win the assignment.  bt holds per chunk of
+// 32 centroids the 32 b_j and then the 32 1 / t_j (one 256-byte run, which
+// the assignment loads with the chunk's tiles).
 template <int D>
 __global__ __launch_bounds__(256) void wprep_kernel(const float* __restrict__ gram, const float* __restrict__ cent,
                                                     _Float16* __restrict__ whi, _Float16* __restrict__ wlo,
                                                     float* __restrict__ w32, float* __restrict__ bvec,
-                                                    float* __restrict__ winv, int NB, int NBp) {
+                                                    float* __restrict__ bt, int NB, int NBp) {
   __shared__ float cs[32][D];
   __shared__ float ws[32][D + 1];
   __shared__ float tsc[32];
@@ -158,7 +160,9 @@ __global__ __launch_bounds__(256) void wprep_kernel(const float* __restrict__ gr
     tsc[tid] = pow2i(shc);
     const size_t o = static_cast<size_t>(h) * NBp + j0 + tid;
     bvec[o] = j0 + tid < NB ? b : INFINITY;
-    winv[o] = pow2i(-shc);
+    float* btc = bt + (static_cast<size_t>(h) * (NBp / 32) + blockIdx.x) * 64;
+    btc[tid] = j0 + tid < NB ? b : INFINITY;
+    btc[32 + tid] = pow2i(-shc);
   }
   __syncthreads();
   for (int e = tid; e < 32 * D; e += 256) {
@@ -175,22 +179,26 @@ __global__ __launch_bounds__(256) void wprep_kernel(const float* __restrict__ gr
 // One workgroup per 128 keys (4 waves of 32).  Each lane holds its key's
 // dims 16s + 8hl..+7 in registers as fp16, scaled by the key's own power of
 // two s_k (exact for bf16 keys).  Centroid chunks of 32 (W_j t_j hi and lo
-// tiles, swizzled) go through LDS; S^T = W K^T puts the 16 clusters
-// 32c + acc_row(r, hl) of this lane's key in its registers, both terms in one
-// accumulation chain, so 2 k.G c_j = acc / (t_j s_k) to about fp32 accuracy
-// (the unscaling is exact) and the running maximum of 2 k.G c_j - b_j stays
-// in-lane; the halves merge last.
+// tiles, swizzled, and the chunk's b_j and 1 / t_j) stream into a ring of two
+// LDS slots with buffer loads straight into LDS (one chunk in flight, four
+// workgroups per CU).  S^T = W K^T puts the 16 clusters 32c + acc_row(r, hl)
+// of this lane's key in its registers, both terms in one accumulation chain,
+// so 2 k.G c_j = acc / (t_j s_k) to about fp32 accuracy (the unscaling is
+// exact) and the running maximum of 2 k.G c_j - b_j stays in-lane; the
+// halves merge last.
 template <int D>
-__global__ __launch_bounds__(256) void assign_bf16_kernel(const uint16_t* __restrict__ k,
-                                                          const _Float16* __restrict__ whi,
-                                                          const _Float16* __restrict__ wlo,
-                                                          const float* __restrict__ bvec,
-                                                          const float* __restrict__ winv,
-                                                          int* __restrict__ labels, int N, int NBp) {
+__global__ __launch_bounds__(256, 4) void assign_bf16_kernel(const uint16_t* __restrict__ k,
+                                                             const _Float16* __restrict__ whi,
+                                                             const _Float16* __restrict__ wlo,
+                                                             const float* __restrict__ bt,
+                                                             int* __restrict__ labels, int N, int NBp) {
   constexpr int kKS = D / 16, kCpr = D / 8;
-  __shared__ __attribute__((aligned(16))) _Float16 th[32 * D];
-  __shared__ __attribute__((aligned(16))) _Float16 tl[32 * D];
-  __shared__ float bs[32], ts[32];
+  constexpr int kTile = 32 * D;                  // fp16 elements of a hi (or lo) tile
+  constexpr int kLoads = kTile * 2 / 16 / 256;   // 16-byte loads per lane per tile
+  static_assert(kLoads >= 1 && kTile * 2 % (16 * 256) == 0, "tile not divisible");
+  constexpr int kSlot = 2 * kTile + 128;         // hi, lo, then 64 floats of (b, 1/t)
+  __shared__ __attribute__((aligned(1024))) _Float16 slot0[kSlot];
+  __shared__ __attribute__((aligned(1024))) _Float16 slot1[kSlot];
   const int h = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int hl = lane >> 5, col = lane & 31;
@@ -223,60 +231,79 @@ __global__ __launch_bounds__(256) void assign_bf16_kernel(const uint16_t* __rest
       for (int e = 0; e < 8; ++e) kf[s][e] = static_cast<_Float16>(x[s][e] * sf);
     kinv = pow2i(-sh);
   }
+  const int nc = NBp / 32;
   const _Float16* wh = whi + static_cast<size_t>(h) * NBp * D;
   const _Float16* wl = wlo + static_cast<size_t>(h) * NBp * D;
-  float best = -INFINITY;
-  int bj = 0;
-  // the next chunk is loaded into registers while this one is multiplied
-  constexpr int kPerThread = 32 * kCpr / 256;
-  static_assert(32 * kCpr % 256 == 0, "chunk not divisible");
-  u32x4 nh[kPerThread], nl[kPerThread];
-  float nb = 0.f, nt = 0.f;
-  auto fetch = [&](int c) {
+  const float* bth = bt + static_cast<size_t>(h) * nc * 64;
+  // each lane's byte offset inside a tile: the chunk that belongs at its
+  // slot of the swizzled layout
+  uint32_t off[kLoads];
 #pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int e = tid + 256 * i, r = e / kCpr, ch = e % kCpr;
-      const size_t g = (static_cast<size_t>(32 * c + r) * D) + ch * 8;
-      nh[i] = *reinterpret_cast<const u32x4*>(wh + g);
-      nl[i] = *reinterpret_cast<const u32x4*>(wl + g);
+  for (int i = 0; i < kLoads; ++i) {
+    const int pc = (wave * kLoads + i) * 64 + lane;
+    const int r = pc / kCpr;
+    off[i] = static_cast<uint32_t>(r * D + ((pc % kCpr) ^ swz<kCpr>(r)) * 8) * 2u;
+  }
+  auto issue = [&](int c, _Float16* dst) __attribute__((always_inline)) {
+    const size_t base = static_cast<size_t>(32 * c) * D;
+    const __amdgpu_buffer_rsrc_t rh =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(wh + base), 0, kTile * 2, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rl =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<_Float16*>(wl + base), 0, kTile * 2, kRsrcWord3);
+#pragma unroll
+    for (int i = 0; i < kLoads; ++i) {
+      const int blk = wave * kLoads + i;
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rh, (lvoid*)(dst + blk * 512), 16, static_cast<int>(off[i]), 0, 0, 0);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rl, (lvoid*)(dst + kTile + blk * 512), 16, static_cast<int>(off[i]), 0,
+                                               0, 0);
     }
-    if (tid < 32) {
-      nb = bvec[static_cast<size_t>(h) * NBp + 32 * c + tid];
-      nt = winv[static_cast<size_t>(h) * NBp + 32 * c + tid];
+    if (wave == 0) {  // the chunk's 32 b_j then 32 1 / t_j, one dword per lane
+      const __amdgpu_buffer_rsrc_t rb =
+          __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(bth + 64 * c), 0, 256, kRsrcWord3);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lvoid*)(dst + 2 * kTile), 4, 4 * lane, 0, 0, 0);
     }
   };
-  fetch(0);
-  for (int c = 0; c < NBp / 32; ++c) {
-    __syncthreads();
-#pragma unroll
-    for (int i = 0; i < kPerThread; ++i) {
-      const int e = tid + 256 * i, r = e / kCpr, ch = e % kCpr;
-      const int dst = r * D + (ch ^ swz<kCpr>(r)) * 8;
-      *reinterpret_cast<u32x4*>(&th[dst]) = nh[i];
-      *reinterpret_cast<u32x4*>(&tl[dst]) = nl[i];
-    }
-    if (tid < 32) {
-      bs[tid] = nb;
-      ts[tid] = nt;
-    }
-    __syncthreads();
-    if (c + 1 < NBp / 32) fetch(c + 1);
+  float best = -INFINITY;
+  int bj = 0;
+  auto body = [&](int c, const _Float16* cur) __attribute__((always_inline)) {
+    const char* th = reinterpret_cast<const char*>(cur);
+    const char* tl = reinterpret_cast<const char*>(cur + kTile);
+    const float* bs = reinterpret_cast<const float*>(cur + 2 * kTile);
     f32x16 acc = f32x16{};
 #pragma unroll
     for (int s = 0; s < kKS; ++s) {
-      const int o = col * D + ((2 * s + hl) ^ swz<kCpr>(col)) * 8;
-      acc = mfma32(*reinterpret_cast<const f16x8*>(&th[o]), kf[s], acc);
-      acc = mfma32(*reinterpret_cast<const f16x8*>(&tl[o]), kf[s], acc);
+      const int o = col * (2 * D) + ((2 * s + hl) ^ swz<kCpr>(col)) * 16;
+      acc = mfma32(*reinterpret_cast<const f16x8*>(th + o), kf[s], acc);
+      acc = mfma32(*reinterpret_cast<const f16x8*>(tl + o), kf[s], acc);
     }
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int jr = acc_row(r, hl);
-      const float v = acc[r] * ts[jr] * kinv - bs[jr];   // the two products by powers of two are exact
+      const float v = acc[r] * bs[32 + jr] * kinv - bs[jr];  // the two products by powers of two are exact
       if (v > best) {  // rows ascend with r: the first maximum is the lowest index
         best = v;
         bj = 32 * c + jr;
       }
     }
+  };
+  // chunk c lives in slot c % 2; before chunk c is read, every wave has
+  // finished chunk c - 1, whose slot is then refilled with chunk c + 1
+  issue(0, slot0);
+  int c = 0;
+  for (; c + 1 < nc; c += 2) {
+    wait_vm<0>();
+    barrier_lds();
+    issue(c + 1, slot1);
+    body(c, slot0);
+    wait_vm<0>();
+    barrier_lds();
+    if (c + 2 < nc) issue(c + 2, slot0);
+    body(c + 1, slot1);
+  }
+  if (c < nc) {
+    wait_vm<0>();
+    barrier_lds();
+    body(c, slot0);
   }
   const float ob = __shfl_xor(best, 32);
   const int oj = __shfl_xor(bj, 32);
@@ -477,7 +504,7 @@ __global__ __launch_bounds__(D) void seg_combine_kernel(const double* __restrict
 
 struct KmeansWs {
   _Float16 *whi, *wlo;
-  float *w32, *bvec, *bmax, *winv;
+  float *w32, *bvec, *bmax, *bt;
   int *hist, *rank, *offs;
   double* part;
   size_t total;
@@ -493,12 +520,12 @@ KmeansWs kmeans_ws_layout(const Problem& p, void* base) {
   const size_t sizes[] = {al256(2 * H * NBp * D), al256(2 * H * NBp * D), al256(4 * H * NBp * D),
                           al256(4 * H * NBp), al256(4 * H * p.nb), al256(4 * H * nch * p.nb),
                           al256(4 * H * static_cast<size_t>(p.tokens)), al256(4 * H * p.nb),
-                          al256(8 * H * nseg * 2 * D), al256(4 * H * NBp)};
+                          al256(8 * H * nseg * 2 * D), al256(8 * H * NBp)};
   KmeansWs w{};
   char* b = static_cast<char*>(base);
   size_t off = 0;
   void** ptrs[] = {(void**)&w.whi, (void**)&w.wlo, (void**)&w.w32, (void**)&w.bvec, (void**)&w.bmax,
-                   (void**)&w.hist, (void**)&w.rank, (void**)&w.offs, (void**)&w.part, (void**)&w.winv};
+                   (void**)&w.hist, (void**)&w.rank, (void**)&w.offs, (void**)&w.part, (void**)&w.bt};
   for (int i = 0; i < 10; ++i) {
     if (b != nullptr) *ptrs[i] = b + off;
     off += sizes[i];
@@ -523,11 +550,11 @@ hipError_t launch_kmeans_t(const Problem& p, const void* k, const float* gram, i
   }
   for (int it = 0; it < iters; ++it) {
     hipLaunchKernelGGL((wprep_kernel<D>), dim3(NBp / 32, H), dim3(256), 0, stream, gram, cent, w.whi, w.wlo,
-                       w.w32, w.bvec, w.winv, NB, NBp);
+                       w.w32, w.bvec, w.bt, NB, NBp);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (p.dtype == 0)
       hipLaunchKernelGGL((assign_bf16_kernel<D>), dim3((N + kAssignRows - 1) / kAssignRows, H), dim3(256), 0,
-                         stream, static_cast<const uint16_t*>(k), w.whi, w.wlo, w.bvec, w.winv, labels, N, NBp);
+                         stream, static_cast<const uint16_t*>(k), w.whi, w.wlo, w.bt, labels, N, NBp);
     else
       hipLaunchKernelGGL((assign_f32_kernel<D>), dim3((N + 255) / 256, H), dim3(256), 0, stream,
                          static_cast<const float*>(k), w.w32, w.bvec, labels, N, NB, NBp);

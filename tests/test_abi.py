@@ -76,12 +76,13 @@ def test_workspace_sizes():
     assert B.workspace_bytes(p, B.OP_GRAM) == al(4 * 40 * 37 * 128 * 128)
     assert B.workspace_bytes(prob(heads=40, grid=(21, 45, 80), b=128, dtype=1), B.OP_GRAM) == 0
     # k-means: 2 G c split (2 x fp16) and fp32, b, block maxima, chunk histograms, ranks, offsets,
-    # fp64 run sums of the mean segments (two per 256 sorted positions), per-centroid unscale factors
+    # fp64 run sums of the mean segments (two per 256 sorted positions), then per chunk of 32
+    # centroids their b and unscale factors together (what the assignment loads with the chunk)
     nch = -(-75600 // 256)
     assert B.workspace_bytes(p, B.OP_KMEANS) == (2 * al(2 * 40 * nbp * 128) + al(4 * 40 * nbp * 128)
                                                  + al(4 * 40 * nbp) + al(4 * 40 * 591) + al(4 * 40 * nch * 591)
                                                  + al(4 * 40 * 75600) + al(4 * 40 * 591)
-                                                 + al(8 * 40 * nch * 2 * 128) + al(4 * 40 * nbp))
+                                                 + al(8 * 40 * nch * 2 * 128) + al(8 * 40 * nbp))
     # cluster attention: k and v in the padded cluster layout, starts, sub-tile tables
     npad = -(-(75600 + 31 * 591) // 32) * 32
     rows = 40 * 591
