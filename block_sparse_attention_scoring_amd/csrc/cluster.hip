@@ -367,10 +367,18 @@ __global__ __launch_bounds__(64) void chunk_scan_kernel(int* __restrict__ hist, 
   if (j >= NB) return;
   int* p = hist + static_cast<size_t>(h) * nch * NB + j;
   int run = 0;
-  for (int c = 0; c < nch; ++c) {
-    const int v = p[static_cast<size_t>(c) * NB];
-    p[static_cast<size_t>(c) * NB] = run;
-    run += v;
+  // batches of loads first, then their stores: the loads of a batch are in
+  // flight together instead of each waiting behind the previous store
+  constexpr int kB = 16;
+  for (int c0 = 0; c0 < nch; c0 += kB) {
+    int v[kB];
+#pragma unroll
+    for (int u = 0; u < kB; ++u) v[u] = c0 + u < nch ? p[static_cast<size_t>(c0 + u) * NB] : 0;
+#pragma unroll
+    for (int u = 0; u < kB; ++u) {
+      if (c0 + u < nch) p[static_cast<size_t>(c0 + u) * NB] = run;
+      run += v[u];
+    }
   }
   sizes[static_cast<size_t>(h) * NB + j] = run;
 }
