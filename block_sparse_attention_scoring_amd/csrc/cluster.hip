@@ -140,13 +140,27 @@ __global__ __launch_bounds__(256) void wprep_kernel(const float* __restrict__ gr
     cs[j][d] = j0 + j < NB ? cent[(static_cast<size_t>(h) * NB + j0 + j) * D + d] : 0.f;
   }
   __syncthreads();
-  for (int e = tid; e < 32 * D; e += 256) {
-    const int j = e / D, d = e % D;
-    float acc = 0.f;
-#pragma unroll 8
-    for (int x = 0; x < D; ++x) acc = fmaf(g[x * D + d], cs[j][x], acc);  // G symmetric: G[d][x] = G[x][d]
-    ws[j][d] = acc;
-    w32[(static_cast<size_t>(h) * NBp + j0 + j) * D + d] = 2.f * acc;
+  {
+    // thread (grp, d) takes dim d of centroids grp, grp + kG, ...: each G
+    // element is read once per group and used for all its centroids
+    constexpr int kG = 256 / D, kJ = 32 / kG;
+    static_assert(256 % D == 0 && 32 % kG == 0, "threads per dim group");
+    const int d = tid % D, grp = tid / D;
+    float acc[kJ];
+#pragma unroll
+    for (int m = 0; m < kJ; ++m) acc[m] = 0.f;
+#pragma unroll 4
+    for (int x = 0; x < D; ++x) {
+      const float gv = g[x * D + d];  // G symmetric: G[d][x] = G[x][d]
+#pragma unroll
+      for (int m = 0; m < kJ; ++m) acc[m] = fmaf(gv, cs[grp + kG * m][x], acc[m]);
+    }
+#pragma unroll
+    for (int m = 0; m < kJ; ++m) {
+      const int j = grp + kG * m;
+      ws[j][d] = acc[m];
+      w32[(static_cast<size_t>(h) * NBp + j0 + j) * D + d] = 2.f * acc[m];
+    }
   }
   __syncthreads();
   if (tid < 32) {
