@@ -33,23 +33,26 @@ namespace rsa {
 namespace {
 
 constexpr int kGramChunk = 2048;  // tokens per partial Gram matrix
-constexpr int kGramStage = 64;    // tokens staged in LDS at a time
+constexpr int kGramStage = 128;   // tokens staged in LDS at a time
 constexpr int kHistChunk = 256;   // tokens per histogram chunk
 constexpr int kAssignRows = 128;  // keys per assignment workgroup
 constexpr int kSeg = 256;         // sorted positions per mean segment
 
 // ---------------------------------------------------------------- gram
 // Partial Q^T Q of one chunk of kGramChunk tokens, bf16 input.  The chunk is
-// staged 64 tokens at a time in LDS transposed (dim-major), so that both
-// operands of a 32x32x16 product (8 consecutive tokens of one dim per lane)
-// are single 16-byte reads.  Wave w owns output tiles w*kPerWave.. of the
-// (D/32)^2 tiles of G.
+// staged kGramStage tokens at a time in LDS transposed (dim-major), so that
+// both operands of a 32x32x16 product (8 consecutive tokens of one dim per
+// lane) are single 16-byte reads.  Each thread stages an 8-token x 8-dim
+// block: eight 16-byte loads (one per token), a transpose in registers (byte
+// selects), eight 16-byte LDS writes (one per dim).  Wave w owns output tiles
+// w*kPerWave.. of the (D/32)^2 tiles of G.
 template <int D>
 __global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t* __restrict__ q,
                                                         float* __restrict__ part, int N, int nchunk) {
   constexpr int kT = D / 32;                // tiles per side
   constexpr int kPerWave = kT * kT / 4;     // tiles per wave
-  constexpr int kStride = kGramStage + 8;   // LDS row pitch in tokens (bank spread)
+  constexpr int kStride = kGramStage + 8;   // LDS row pitch in tokens (bank spread; 16-byte rows stay aligned)
+  static_assert(kStride * 2 % 16 == 0 && kGramChunk % kGramStage == 0, "aligned rows, whole stages");
   __shared__ __attribute__((aligned(16))) uint16_t qt[D * kStride];
   const int c = blockIdx.x, h = blockIdx.y, tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6, hl = lane >> 5, col = lane & 31;
@@ -60,14 +63,27 @@ __global__ __launch_bounds__(256) void gram_bf16_kernel(const uint16_t* __restri
   for (int i = 0; i < kPerWave; ++i) acc[i] = f32x16{};
   for (int s0 = t0; s0 < t1; s0 += kGramStage) {
     __syncthreads();
-    for (int e = tid; e < kGramStage * D / 8; e += 256) {
-      const int t = e / (D / 8), d8 = (e % (D / 8)) * 8;
-      u32x4 x = s0 + t < t1 ? *reinterpret_cast<const u32x4*>(qh + static_cast<size_t>(s0 + t) * D + d8)
-                            : u32x4{0, 0, 0, 0};
+    for (int e = tid; e < (kGramStage / 8) * (D / 8); e += 256) {
+      const int g = e / (D / 8), d8 = (e % (D / 8)) * 8;  // tokens s0 + 8g.., dims d8..
+      u32x4 x[8];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int t = s0 + 8 * g + u;
+        x[u] = t < t1 ? *reinterpret_cast<const u32x4*>(qh + static_cast<size_t>(t) * D + d8) : u32x4{0, 0, 0, 0};
+      }
+      // word w of x[u] holds dims d8 + 2w (low half) and d8 + 2w + 1 (high
+      // half) of token u; word m of row y[dd] holds tokens 2m (low) and
+      // 2m + 1 (high) of dim d8 + dd
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        qt[(d8 + 2 * w) * kStride + t] = static_cast<uint16_t>(x[w] & 0xffffu);
-        qt[(d8 + 2 * w + 1) * kStride + t] = static_cast<uint16_t>(x[w] >> 16);
+        u32x4 lo, hi;
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          lo[m] = __builtin_amdgcn_perm(x[2 * m + 1][w], x[2 * m][w], 0x05040100u);  // low halves
+          hi[m] = __builtin_amdgcn_perm(x[2 * m + 1][w], x[2 * m][w], 0x07060302u);  // high halves
+        }
+        *reinterpret_cast<u32x4*>(&qt[(d8 + 2 * w) * kStride + 8 * g]) = lo;
+        *reinterpret_cast<u32x4*>(&qt[(d8 + 2 * w + 1) * kStride + 8 * g]) = hi;
       }
     }
     __syncthreads();
