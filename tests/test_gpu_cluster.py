@@ -30,7 +30,8 @@ DEV = "cuda:0"
 
 CASES = {
     # name: (heads, grid, head_dim, block, dtype)
-    "bf16_d128_b128": (2, (6, 20, 83), 128, 128, "bf16"),  # N=9960: 5 Gram chunks, NB=78
+    "bf16_d128_b128": (2, (6, 20, 83), 128, 128, "bf16"),  # N=9960: 5 Gram chunks, NB=78 (3 centroid chunks)
+    "two_chunks_bf16_d128_b128": (1, (5, 16, 80), 128, 128, "bf16"),  # N=6400, NB=50: an even number (2) of centroid chunks
     "bf16_d128_b64": (2, (3, 10, 41), 128, 64, "bf16"),    # N=1230, NB=20, last block 14
     "bf16_d64_b64": (3, (4, 9, 37), 64, 64, "bf16"),       # N=1332, NB=21
     "fp32_d64_b64": (1, (4, 8, 8), 64, 64, "fp32"),        # the tiny shape
